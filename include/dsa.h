@@ -1,0 +1,172 @@
+/*
+ * libdsa — DeepSeek Sparse Attention (DSA) hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps, as the pages describe them:
+ *   1. lightning indexer: every past token of a query gets a score, the per-head weighted sum
+ *      of ReLU(query-head . key) over the indexer heads, one key row per token
+ *      ("How GLM5.3 Sparse Attention Affects HBM Memory Usage", How it works / Model;
+ *      "DeepSeek Sparse Attention" technique page, In the code: ReLU(q.k) weighted sums);
+ *   2. per-query causal top-k (index_topk = 2048; below k visible tokens attention stays dense),
+ *      one selection shared by all attention heads (same page and section);
+ *   3. sparse MLA in MQA mode: every query head attends with softmax over only the selected
+ *      latent rows; the key is the whole latent+rope row, the value its leading d_v columns
+ *      (same page and section; the 120.8 FLOP/B decode intensity at 64 heads fixes this layout).
+ *   IndexShare (same page, How it works / IndexShare): one indexer + top-k pass serves a group
+ *   of layers; its cached indices are reused by the other layers of the group.
+ *
+ * Conventions shared by every call
+ *   - Ragged batch (dsa_batch): sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *     and key / latent rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; L_b = its context length.
+ *     Query j of sequence b (nq_b new queries, nq_b <= L_b) sits at position p = L_b - nq_b + j
+ *     and sees sequence positions 0..p (itself included).
+ *   - All tensors are dense row-major device buffers owned by the caller. The library never
+ *     allocates, frees or synchronises on a call path; each call only enqueues work on `stream`
+ *     and returns. Scratch memory comes from a caller-provided workspace whose size is given by
+ *     dsa_workspace_size(). The library keeps no mutable global state.
+ *   - All argument checks run on the host before anything is enqueued; a non-zero status means
+ *     nothing was launched. Device-resident values (cu_seqlens) cannot be checked without a
+ *     synchronisation: the caller guarantees they are consistent with the host-side sizes, and
+ *     every kernel clamps its reads to total_q / total_k / ld so inconsistent values give wrong
+ *     results, never out-of-bounds accesses. dsa_check_batch() validates them on demand (it
+ *     synchronises the stream).
+ *   - A failed kernel launch returns DSA_ERR_HIP; the HIP error stays readable through
+ *     hipGetLastError().
+ *   - Supported shapes: bf16 with (d_qk, d_v, index_head_dim) = (576, 512, 128),
+ *     n_heads a multiple of 64, index_n_heads 32 or 64; fp32 with d_qk <= 1024, d_v <= d_qk,
+ *     index_head_dim <= 256, n_heads <= 1024, index_n_heads <= 128. Other combinations return
+ *     DSA_ERR_UNSUPPORTED.
+ */
+#ifndef LIBDSA_DSA_H
+#define LIBDSA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes            */
+  DSA_ERR_UNSUPPORTED = 2,   /* valid but not compiled: dims / dtype combination           */
+  DSA_ERR_WORKSPACE = 3,     /* workspace null or smaller than dsa_workspace_size()        */
+  DSA_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed                 */
+  DSA_ERR_BATCH = 5          /* dsa_check_batch(): cu_seqlens inconsistent with the sizes  */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+/* Ragged batch description. Host integers plus two device arrays. */
+typedef struct {
+  int32_t batch;                 /* B >= 1                                                    */
+  int32_t total_q;               /* T = rows of q, q_idx, w, out, lse, indices, scores        */
+  int64_t total_k;               /* rows of kv and k_idx = cu_seqlens_k[B]                     */
+  int32_t max_seqlen_q;          /* max_b nq_b (>= 1)                                          */
+  int32_t max_seqlen_k;          /* max_b L_b (>= 1); row length bound for scores             */
+  const int32_t* cu_seqlens_q;   /* device [B+1], cu_seqlens_q[0] = 0, cu_seqlens_q[B] = T     */
+  const int64_t* cu_seqlens_k;   /* device [B+1], cu_seqlens_k[0] = 0, cu_seqlens_k[B] = total_k */
+} dsa_batch;
+
+/* Step 1 — lightning indexer ("How GLM5.3 Sparse Attention Affects HBM Memory Usage",
+ * How it works / Model).
+ *   scores[t * ld_scores + s] = sum_j w[t, j] * max(0, sum_c q_idx[t, j, c] * k_idx[cu_k[b] + s, c])
+ * for every query t (of sequence b, position p) and s = 0..p. Entries s > p are not written.
+ *   q_idx  [T, index_n_heads, index_head_dim]  dtype
+ *   k_idx  [total_k, index_head_dim]           dtype (one key row per token, shared by heads)
+ *   w      [T, index_n_heads]                  fp32
+ *   scores [T, ld_scores]                      fp32, ld_scores >= max_seqlen_k
+ * Products are accumulated in fp32; integer-valued inputs whose sums stay below 2^24 give
+ * exact scores. */
+dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx,
+                              const float* w, int32_t index_n_heads, int32_t index_head_dim,
+                              dsa_dtype dtype, float* scores, int64_t ld_scores,
+                              hipStream_t stream);
+
+/* Step 2 — causal top-k (same page and section: top-k 2048, dense below k).
+ * For query t at position p: if p + 1 <= index_topk, indices[t] = 0, 1, .., p, then -1;
+ * otherwise the index_topk positions with the largest scores among 0..p, where scores compare
+ * as real numbers (-0.0 == +0.0) and an equal score goes to the lower position. The selected
+ * positions are written in ascending order.
+ *   scores  [T, ld_scores] fp32 (only s <= p is read)
+ *   indices [T, index_topk] int32, sequence-local positions
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 bytes / NULL when that is 0)
+ * Scores must not be NaN. */
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
+                    int32_t index_topk, int32_t* indices, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Step 3 — sparse MLA forward in MQA mode (same page and section).
+ *   z_s = softmax_scale * sum_{c < d_qk} q[t, h, c] * kv[cu_k[b] + s, c]   for s in indices[t]
+ *   out[t, h, :] = sum_s softmax(z)_s * kv[cu_k[b] + s, 0:d_v];  lse[t, h] = ln sum_s exp(z_s)
+ *   q       [T, n_heads, d_qk]   dtype
+ *   kv      [total_k, d_qk]      dtype (latent + rope row; its first d_v columns are the value)
+ *   indices [T, index_topk]      int32 sequence-local positions in any order; entries < 0 are
+ *                                skipped; entries >= L_b are skipped; duplicates count twice.
+ *   out     [T, n_heads, d_v]    dtype;  lse [T, n_heads] fp32 or NULL.
+ * A query with no valid index gets out = 0 and lse = -inf. Softmax statistics and the output
+ * accumulator are fp32; probabilities are rounded to bf16 for the value product on the bf16
+ * path. */
+dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void* kv,
+                              const int32_t* indices, int32_t index_topk, int32_t n_heads,
+                              int32_t d_qk, int32_t d_v, float softmax_scale, dsa_dtype dtype,
+                              void* out, float* lse, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Inputs of the three steps, for the fused call. */
+typedef struct {
+  const void* q_idx;             /* [T, index_n_heads, index_head_dim]                         */
+  const void* k_idx;             /* [total_k, index_head_dim]                                  */
+  const float* w;                /* [T, index_n_heads]                                         */
+  int32_t index_n_heads;
+  int32_t index_head_dim;
+  int32_t index_topk;
+  const void* q;                 /* [T, n_heads, d_qk]                                         */
+  const void* kv;                /* [total_k, d_qk]                                            */
+  int32_t n_heads;
+  int32_t d_qk;
+  int32_t d_v;
+  float softmax_scale;
+  dsa_dtype dtype;
+} dsa_forward_args;
+
+/* Whole path with IndexShare (same page, How it works / IndexShare).
+ * compute_indices = 1: indexer + top-k write shared_indices [T, index_topk], then sparse MLA
+ *                      reads them (q_idx, k_idx, w must be valid).
+ * compute_indices = 0: shared_indices is read as cached by an earlier call of the group;
+ *                      q_idx / k_idx / w are ignored and may be NULL.
+ * The workspace holds the [T, max_seqlen_k] fp32 score matrix plus the top-k and split-KV
+ * scratch: dsa_workspace_size(DSA_OP_FORWARD, ...) bytes. */
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* args,
+                       int32_t* shared_indices, int32_t compute_indices, void* out, float* lse,
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+typedef enum {
+  DSA_OP_INDEXER = 0,            /* needs no workspace                                         */
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA = 2,
+  DSA_OP_FORWARD = 3
+} dsa_op;
+
+/* Workspace bytes needed by `op` for this batch (host sizes only). 0 on invalid arguments. */
+size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,
+                          int32_t n_heads, int32_t d_v);
+
+/* Copies cu_seqlens to the host (synchronising `stream`) and checks them against the host
+ * sizes: monotone, cu_q[0] = cu_k[0] = 0, cu_q[B] = total_q, cu_k[B] = total_k,
+ * 1 <= nq_b <= L_b, max_b nq_b <= max_seqlen_q, max_b L_b <= max_seqlen_k.
+ * Returns DSA_OK or DSA_ERR_BATCH (DSA_ERR_HIP if a copy fails). */
+dsa_status dsa_check_batch(const dsa_batch* batch, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDSA_DSA_H */

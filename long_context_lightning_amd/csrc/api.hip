@@ -1,0 +1,230 @@
+// C ABI of libdsa: host-side validation, workspace layout and launch sequencing.
+// Every check runs before anything is enqueued; calls only enqueue work on the caller's stream.
+#include <vector>
+
+#include "../../include/dsa.h"
+#include "kernels.hpp"
+
+using dsa::Batch;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool batch_ok(const dsa_batch* b) {
+  return b && b->batch >= 1 && b->total_q >= 0 && b->total_k >= 0 && b->max_seqlen_q >= 1 &&
+         b->max_seqlen_k >= 1 && b->cu_seqlens_q && b->cu_seqlens_k &&
+         (int64_t)b->max_seqlen_q <= (int64_t)b->max_seqlen_k &&
+         b->total_k <= (int64_t)b->batch * b->max_seqlen_k &&
+         (int64_t)b->total_q <= (int64_t)b->batch * b->max_seqlen_q &&
+         b->total_q <= b->total_k;
+}
+
+Batch to_batch(const dsa_batch* b) {
+  Batch r;
+  r.nseq = b->batch;
+  r.total_q = b->total_q;
+  r.total_k = b->total_k;
+  r.max_q = b->max_seqlen_q;
+  r.max_k = b->max_seqlen_k;
+  r.cu_q = b->cu_seqlens_q;
+  r.cu_k = b->cu_seqlens_k;
+  return r;
+}
+
+dsa_status from_hip(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+// Indexer inputs; the score buffer is checked by the caller.
+dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_idx, const float* w,
+                         int32_t hi, int32_t di, dsa_dtype dt, int64_t ld) {
+  if (!batch_ok(b) || !q_idx || !k_idx || !w || hi <= 0 || di <= 0 || ld < b->max_seqlen_k)
+    return DSA_ERR_INVALID_ARG;
+  if (dt == DSA_BF16) {
+    if (di != 128 || (hi != 32 && hi != 64)) return DSA_ERR_UNSUPPORTED;
+  } else if (dt == DSA_F32) {
+    if (di > 256 || hi > 128) return DSA_ERR_UNSUPPORTED;
+  } else {
+    return DSA_ERR_INVALID_ARG;
+  }
+  return DSA_OK;
+}
+
+dsa_status check_mla(const dsa_batch* b, const void* q, const void* kv, const int32_t* indices,
+                     int32_t k, int32_t h, int32_t dqk, int32_t dv, float scale, dsa_dtype dt,
+                     const void* out) {
+  if (!batch_ok(b) || !q || !kv || !indices || !out || k <= 0 || h <= 0 || dqk <= 0 ||
+      dv <= 0 || dv > dqk || !(scale == scale))
+    return DSA_ERR_INVALID_ARG;
+  if (dt == DSA_BF16) {
+    if (dqk != 576 || dv != 512 || h % 64 != 0) return DSA_ERR_UNSUPPORTED;
+  } else if (dt == DSA_F32) {
+    if (dqk > 1024 || h > 1024 || k > dsa::kMaxF32TopK) return DSA_ERR_UNSUPPORTED;
+  } else {
+    return DSA_ERR_INVALID_ARG;
+  }
+  return DSA_OK;
+}
+
+size_t mla_ws(const dsa_batch* b, int32_t k, int32_t h, dsa_dtype dt) {
+  if (dt != DSA_BF16) return 0;
+  return dsa::plan_sparse_mla_bf16(to_batch(b), k, h).workspace;
+}
+
+size_t scores_bytes(const dsa_batch* b) {
+  return align_up((size_t)b->total_q * (size_t)b->max_seqlen_k * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx,
+                              const float* w, int32_t index_n_heads, int32_t index_head_dim,
+                              dsa_dtype dtype, float* scores, int64_t ld_scores,
+                              hipStream_t stream) {
+  if (!scores) return DSA_ERR_INVALID_ARG;
+  dsa_status st = check_indexer(batch, q_idx, k_idx, w, index_n_heads, index_head_dim, dtype,
+                                ld_scores);
+  if (st != DSA_OK) return st;
+  if (batch->total_q == 0 || batch->total_k == 0) return DSA_OK;
+  const Batch b = to_batch(batch);
+  if (dtype == DSA_BF16)
+    return from_hip(dsa::launch_indexer_bf16(b, q_idx, k_idx, w, index_n_heads, scores,
+                                             ld_scores, stream));
+  return from_hip(dsa::launch_indexer_f32(b, (const float*)q_idx, (const float*)k_idx, w,
+                                          index_n_heads, index_head_dim, scores, ld_scores,
+                                          stream));
+}
+
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
+                    int32_t index_topk, int32_t* indices, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!batch_ok(batch) || !scores || !indices || index_topk <= 0 ||
+      ld_scores < batch->max_seqlen_k)
+    return DSA_ERR_INVALID_ARG;
+  const Batch b = to_batch(batch);
+  const size_t need = dsa::topk_workspace_bytes(b, index_topk);
+  if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (batch->total_q == 0) return DSA_OK;
+  return from_hip(dsa::launch_topk(b, scores, ld_scores, index_topk, indices, workspace, stream));
+}
+
+dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void* kv,
+                              const int32_t* indices, int32_t index_topk, int32_t n_heads,
+                              int32_t d_qk, int32_t d_v, float softmax_scale, dsa_dtype dtype,
+                              void* out, float* lse, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  dsa_status st = check_mla(batch, q, kv, indices, index_topk, n_heads, d_qk, d_v,
+                            softmax_scale, dtype, out);
+  if (st != DSA_OK) return st;
+  const Batch b = to_batch(batch);
+  if (dtype == DSA_BF16) {
+    const dsa::MlaPlan plan = dsa::plan_sparse_mla_bf16(b, index_topk, n_heads);
+    if (plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace)) return DSA_ERR_WORKSPACE;
+    if (batch->total_q == 0) return DSA_OK;
+    return from_hip(dsa::launch_sparse_mla_bf16(b, q, kv, indices, index_topk, n_heads,
+                                                softmax_scale, out, lse, workspace, plan,
+                                                stream));
+  }
+  if (batch->total_q == 0) return DSA_OK;
+  return from_hip(dsa::launch_sparse_mla_f32(b, (const float*)q, (const float*)kv, indices,
+                                             index_topk, n_heads, d_qk, d_v, softmax_scale,
+                                             (float*)out, lse, stream));
+}
+
+size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,
+                          int32_t n_heads, int32_t d_v) {
+  if (!batch_ok(batch) || index_topk <= 0) return 0;
+  const Batch b = to_batch(batch);
+  // only the bf16 (d_v = 512) sparse-MLA kernel splits the selected rows and needs scratch
+  const bool split_kv = n_heads > 0 && n_heads % 64 == 0 && d_v == 512;
+  const size_t mla = split_kv ? mla_ws(batch, index_topk, n_heads, DSA_BF16) : 0;
+  switch (op) {
+    case DSA_OP_INDEXER:
+      return 0;
+    case DSA_OP_TOPK:
+      return dsa::topk_workspace_bytes(b, index_topk);
+    case DSA_OP_SPARSE_MLA:
+      return mla;
+    case DSA_OP_FORWARD:
+      return scores_bytes(batch) + align_up(dsa::topk_workspace_bytes(b, index_topk)) +
+             align_up(mla);
+  }
+  return 0;
+}
+
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_t* shared_indices,
+                       int32_t compute_indices, void* out, float* lse, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
+  if (!a || !shared_indices || (compute_indices != 0 && compute_indices != 1))
+    return DSA_ERR_INVALID_ARG;
+  dsa_status st = check_mla(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,
+                            a->d_qk, a->d_v, a->softmax_scale, a->dtype, out);
+  if (st != DSA_OK) return st;
+  const Batch b = to_batch(batch);
+  const size_t s_bytes = compute_indices ? scores_bytes(batch) : 0;
+  const size_t t_bytes = compute_indices ? align_up(dsa::topk_workspace_bytes(b, a->index_topk)) : 0;
+  const size_t m_bytes = mla_ws(batch, a->index_topk, a->n_heads, a->dtype);
+  const size_t need = s_bytes + t_bytes + m_bytes;
+  if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  float* scores = (float*)ws;
+  const int64_t ld = batch->max_seqlen_k;
+  if (compute_indices) {
+    st = check_indexer(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads, a->index_head_dim,
+                       a->dtype, ld);
+    if (st != DSA_OK) return st;
+  }
+  if (batch->total_q == 0) return DSA_OK;
+  if (compute_indices) {
+    st = dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
+                            a->index_head_dim, a->dtype, scores, ld, stream);
+    if (st != DSA_OK) return st;
+    st = dsa_topk(batch, scores, ld, a->index_topk, shared_indices, ws + s_bytes, t_bytes,
+                  stream);
+    if (st != DSA_OK) return st;
+  }
+  return dsa_sparse_mla_fwd(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,
+                            a->d_qk, a->d_v, a->softmax_scale, a->dtype, out, lse,
+                            ws + s_bytes + t_bytes, m_bytes, stream);
+}
+
+dsa_status dsa_check_batch(const dsa_batch* batch, hipStream_t stream) {
+  if (!batch_ok(batch)) return DSA_ERR_INVALID_ARG;
+  const int B = batch->batch;
+  std::vector<int32_t> cq(B + 1);
+  std::vector<int64_t> ck(B + 1);
+  if (hipStreamSynchronize(stream) != hipSuccess) return DSA_ERR_HIP;
+  if (hipMemcpy(cq.data(), batch->cu_seqlens_q, (B + 1) * sizeof(int32_t),
+                hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ck.data(), batch->cu_seqlens_k, (B + 1) * sizeof(int64_t),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return DSA_ERR_HIP;
+  if (cq[0] != 0 || ck[0] != 0 || cq[B] != batch->total_q || ck[B] != batch->total_k)
+    return DSA_ERR_BATCH;
+  for (int b = 0; b < B; ++b) {
+    const int64_t nq = (int64_t)cq[b + 1] - cq[b];
+    const int64_t L = ck[b + 1] - ck[b];
+    if (nq < 1 || L < nq || nq > batch->max_seqlen_q || L > batch->max_seqlen_k)
+      return DSA_ERR_BATCH;
+  }
+  return DSA_OK;
+}
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or dtype not compiled";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime error";
+    case DSA_ERR_BATCH: return "DSA_ERR_BATCH: cu_seqlens inconsistent with batch sizes";
+  }
+  return "unknown dsa_status";
+}
+
+int32_t dsa_version(void) { return 100; }
+
+}  // extern "C"

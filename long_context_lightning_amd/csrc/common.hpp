@@ -1,0 +1,128 @@
+// Shared device helpers for libdsa (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int WAVE = 64;
+
+// D = A(32x16) * B(16x32) + C on the matrix core. Lane l holds A[l%32][8*(l/32)+e] and
+// B[8*(l/32)+e][l%32] (e = 0..7); result element r of lane l is D[8*(r/4)+4*(l/32)+r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 MFMA result held in element r of lane l.
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// 64-bit transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives element (i & 3) of the 4-element chunk addressed by lane 4*e + (i >> 2),
+// for e = 0..3. If lane j of the group points at row (j >> 2), columns 4*(j & 3)..+3 of a
+// row-major 16-bit matrix, lane i gets column i of those 4 rows.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) char*)(lds_void*)lds_ptr));
+}
+
+// Eight bf16 from two 4 x 16-bit transposed reads (v0 then v1), reinterpreted as one vector.
+__device__ __forceinline__ bf16x8 concat_bf16(i16x4 v0, i16x4 v1) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 both = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane. The LDS destination of lane i is
+// lds_wave_base + 16*i (lds_wave_base must be wave-uniform); completion is tracked by vmcnt.
+__device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait for every outstanding vector-memory, LDS and export operation of this wave.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Order-preserving unsigned key of a float score: a > b (as reals) <=> key(a) > key(b).
+// -0.0 and +0.0 are the same real number and get the same key.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, WAVE));
+  return v;
+}
+
+// Largest b in [0, nseq) with cu[b] <= x (cu ascending, cu[0] <= x).
+template <typename I>
+__device__ __forceinline__ int find_seq(const I* __restrict__ cu, int nseq, int64_t x) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Position of query row t: sequence b, position p (may see 0..p), key base and length.
+struct QueryPos {
+  int b;
+  int64_t p;        // -1 if the row is not a valid query
+  int64_t key_base; // first key row of sequence b
+  int64_t len;      // L_b
+};
+
+__device__ __forceinline__ QueryPos query_pos(const int32_t* __restrict__ cu_q,
+                                              const int64_t* __restrict__ cu_k, int nseq,
+                                              int64_t total_k, int t) {
+  QueryPos r;
+  r.b = find_seq(cu_q, nseq, t);
+  int64_t q0 = cu_q[r.b], q1 = cu_q[r.b + 1];
+  int64_t k0 = cu_k[r.b], k1 = cu_k[r.b + 1];
+  k0 = max((int64_t)0, min(k0, total_k));
+  k1 = max(k0, min(k1, total_k));
+  r.key_base = k0;
+  r.len = k1 - k0;
+  int64_t nq = q1 - q0;
+  r.p = (t >= q0 && t < q1) ? r.len - nq + (t - q0) : -1;
+  if (r.p >= r.len) r.p = r.len - 1;
+  return r;
+}
+
+}  // namespace dsa

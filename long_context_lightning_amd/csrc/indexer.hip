@@ -1,0 +1,284 @@
+// Lightning indexer ("How GLM5.3 Sparse Attention Affects HBM Memory Usage", How it works /
+// Model): the score of past token s for query t is the weighted sum over indexer heads j of
+// ReLU(q_I[t, j] . k_I[s]), one key row per token shared by all heads.
+//
+// bf16 path (index_head_dim = 128, index_n_heads = 32 * HB): the 32 heads of one query form the
+// M dimension of a 32x32x16 MFMA and 32 keys its N dimension, so one MFMA result tile holds
+// one query's 32 heads for 32 keys. The epilogue applies ReLU, scales by w and reduces the
+// heads inside each lane (16 head rows per lane) plus one cross-lane exchange between the two
+// lane halves; lanes 0..31 then hold the 32 finished scores of the tile.
+//
+//  * decode kernel: few queries per sequence. Each wave streams 256 consecutive key rows of the
+//    flattened key cache straight from HBM into registers (B operand), double-buffered, with the
+//    query's heads resident in registers (A operand). Work is laid over the flattened key rows,
+//    so ragged batches with very different lengths need no padding.
+//  * prefill kernel: many queries per sequence (chunked prefill). A workgroup owns 16 queries
+//    (4 per wave, A operands in registers) and walks the causal key range in 64-key tiles staged
+//    in LDS with direct global->LDS loads, double-buffered; each B fragment read from LDS feeds 4
+//    queries' MFMAs.
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int D = 128;                  // index_head_dim on the bf16 path
+constexpr int DEC_KEYS_PER_WAVE = 256;
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
+
+template <int HB>
+__device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
+                                               const __bf16* __restrict__ k_idx,
+                                               const float* __restrict__ w, int t, int64_t kb0,
+                                               int64_t s_beg, int64_t s_end,
+                                               float* __restrict__ srow) {
+  constexpr int HI = 32 * HB;
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  bf16x8 a[HB][8];
+  float wr[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const __bf16* qr = q_idx + ((int64_t)t * HI + hb * 32 + col) * D + half * 8;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) a[hb][st] = *(const bf16x8*)(qr + st * 16);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[hb][r] = w[(int64_t)t * HI + hb * 32 + mfma32_row(r, lane)];
+  }
+
+  const __bf16* kb = k_idx + kb0 * D + half * 8;
+  bf16x8 cur[8], nxt[8];
+  {
+    const int64_t s = min(s_beg + col, s_end - 1);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) cur[st] = *(const bf16x8*)(kb + s * D + st * 16);
+  }
+  for (int64_t s0 = s_beg; s0 < s_end; s0 += 32) {
+    if (s0 + 32 < s_end) {
+      const int64_t s = min(s0 + 32 + col, s_end - 1);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) nxt[st] = *(const bf16x8*)(kb + s * D + st * 16);
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[hb][st], cur[st], acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], fmaxf(acc[r], 0.f), v);
+    }
+    v += __shfl_xor(v, 32, WAVE);
+    const int64_t s = s0 + col;
+    if (half == 0 && s < s_end) srow[s] = v;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) cur[st] = nxt[st];
+  }
+}
+
+// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = query offset j within its sequence.
+template <int HB>
+__global__ __launch_bounds__(256) void indexer_decode_bf16(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
+    const float* __restrict__ w, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
+    float* __restrict__ scores, int64_t ld) {
+  const int wave = threadIdx.x >> 6;
+  const int j = blockIdx.y;
+  int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK + (int64_t)wave * DEC_KEYS_PER_WAVE;
+  const int64_t f_end = min(f + DEC_KEYS_PER_WAVE, total_k);
+  while (f < f_end) {
+    const int b = find_seq(cu_k, nseq, f);
+    const int64_t kb0 = cu_k[b];
+    const int64_t kb1 = min(cu_k[b + 1], total_k);
+    if (kb1 <= f || kb0 > f) break;
+    const int64_t seg_end = min(f_end, kb1);
+    const int q0 = cu_q[b];
+    const int nq = cu_q[b + 1] - q0;
+    if (j < nq && q0 + j < total_q && q0 + j >= 0) {
+      const int t = q0 + j;
+      const int64_t p = (kb1 - kb0) - nq + j;
+      const int64_t s_beg = f - kb0;
+      const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
+      if (s_beg < s_end)
+        decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg, s_end, scores + (int64_t)t * ld);
+    }
+    f = seg_end;
+  }
+}
+
+constexpr int PF_QW = 4;                // queries per wave
+constexpr int PF_WAVES = 4;
+constexpr int PF_QB = PF_QW * PF_WAVES; // queries per workgroup
+constexpr int PF_KT = 64;               // keys per LDS stage
+constexpr int PF_STAGE = PF_KT * D;     // bf16 elements per stage
+
+// grid: x = query blocks of PF_QB over max_seqlen_q, y = sequence, z = key-range splits.
+template <int HB>
+__global__ __launch_bounds__(256, 1) void indexer_prefill_bf16(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
+    const float* __restrict__ w, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
+    float* __restrict__ scores, int64_t ld) {
+  constexpr int HI = 32 * HB;
+  __shared__ __attribute__((aligned(16))) __bf16 ktile[2][PF_STAGE];
+
+  const int b = blockIdx.y;
+  if (b >= nseq) return;
+  const int q0 = cu_q[b];
+  const int nq = cu_q[b + 1] - q0;
+  const int64_t kb0 = cu_k[b];
+  const int64_t kb1 = min(cu_k[b + 1], total_k);
+  const int64_t L = kb1 - kb0;
+  const int jb = blockIdx.x * PF_QB;
+  if (jb >= nq || L <= 0 || q0 < 0 || q0 + nq > total_q) return;
+  const int jcount = min(PF_QB, nq - jb);
+  const int64_t p_first = L - nq + jb;
+  const int64_t nkeys = min(min(p_first + jcount, L), ld);   // keys 0..nkeys-1 are needed
+  if (nkeys <= 0) return;
+  const int64_t ntiles = (nkeys + PF_KT - 1) / PF_KT;
+  const int64_t tile_beg = ntiles * blockIdx.z / gridDim.z;
+  const int64_t tile_end = ntiles * (blockIdx.z + 1) / gridDim.z;
+  if (tile_beg >= tile_end) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  bf16x8 a[PF_QW][HB][8];
+  float wr[PF_QW][HB][16];
+#pragma unroll
+  for (int qi = 0; qi < PF_QW; ++qi) {
+    const int jq = min(jb + wave * PF_QW + qi, nq - 1);
+    const int64_t t = q0 + jq;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const __bf16* qr = q_idx + (t * HI + hb * 32 + col) * D + half * 8;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) a[qi][hb][st] = *(const bf16x8*)(qr + st * 16);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wr[qi][hb][r] = w[t * HI + hb * 32 + mfma32_row(r, lane)];
+    }
+  }
+
+  // Stage layout: key row r occupies 16 slots of 16 B; the slot of 16-B chunk c is c ^ (r & 7),
+  // so the 32 rows read by one B-operand load spread over all LDS banks.
+  auto issue = [&](int64_t ti, int stg) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int slot = c * 256 + tid;
+      const int row = slot >> 4;
+      const int gc = (slot & 15) ^ (row & 7);
+      const int64_t key = min(ti * PF_KT + row, nkeys - 1);
+      global_to_lds16(k_idx + (kb0 + key) * D + gc * 8, &ktile[stg][(c * 256 + wave * 64) * 8]);
+    }
+  };
+
+  issue(tile_beg, 0);
+  for (int64_t ti = tile_beg; ti < tile_end; ++ti) {
+    const int stg = (int)((ti - tile_beg) & 1);
+    wait_all_memory();
+    __syncthreads();
+    if (ti + 1 < tile_end) issue(ti + 1, stg ^ 1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int row = sub * 32 + col;
+      bf16x8 bop[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int chunk = st * 2 + half;
+        bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
+      }
+      const int64_t s = ti * PF_KT + row;
+#pragma unroll
+      for (int qi = 0; qi < PF_QW; ++qi) {
+        float v = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[qi][hb][st], bop[st], acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], fmaxf(acc[r], 0.f), v);
+        }
+        v += __shfl_xor(v, 32, WAVE);
+        const int jq = jb + wave * PF_QW + qi;
+        const int64_t p = p_first + wave * PF_QW + qi;
+        if (half == 0 && jq < nq && s <= p && s < nkeys)
+          scores[(int64_t)(q0 + jq) * ld + s] = v;
+      }
+    }
+  }
+}
+
+// fp32 path: one thread per (query, key); plain FMA loops.
+__global__ __launch_bounds__(256) void indexer_f32(
+    const float* __restrict__ q_idx, const float* __restrict__ k_idx,
+    const float* __restrict__ w, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int HI, int DI,
+    float* __restrict__ scores, int64_t ld) {
+  const int t = blockIdx.y;
+  if (t >= total_q) return;
+  const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, t);
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (qp.p < 0 || s > qp.p || s >= ld) return;
+  const float* kr = k_idx + (qp.key_base + s) * DI;
+  const float* qt = q_idx + (int64_t)t * HI * DI;
+  float acc = 0.f;
+  for (int j = 0; j < HI; ++j) {
+    float d = 0.f;
+    for (int c = 0; c < DI; ++c) d = fmaf(qt[j * DI + c], kr[c], d);
+    acc = fmaf(w[(int64_t)t * HI + j], fmaxf(d, 0.f), acc);
+  }
+  scores[(int64_t)t * ld + s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_idx,
+                               const float* w, int index_n_heads, float* scores, int64_t ld,
+                               hipStream_t stream) {
+  const __bf16* q = (const __bf16*)q_idx;
+  const __bf16* k = (const __bf16*)k_idx;
+  const bool prefill = b.max_q >= PF_QB;
+  if (prefill) {
+    const int qblocks = (b.max_q + PF_QB - 1) / PF_QB;
+    const int64_t base = (int64_t)qblocks * b.nseq;
+    int splits = (int)((1024 + base - 1) / base);
+    splits = std::max(1, std::min(splits, 8));
+    dim3 grid(qblocks, b.nseq, splits);
+    if (index_n_heads == 32)
+      indexer_prefill_bf16<1><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                        b.total_q, b.total_k, scores, ld);
+    else
+      indexer_prefill_bf16<2><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                        b.total_q, b.total_k, scores, ld);
+  } else {
+    dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK), b.max_q);
+    if (index_n_heads == 32)
+      indexer_decode_bf16<1><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                       b.total_q, b.total_k, scores, ld);
+    else
+      indexer_decode_bf16<2><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                       b.total_q, b.total_k, scores, ld);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_f32(const Batch& b, const float* q_idx, const float* k_idx,
+                              const float* w, int index_n_heads, int index_head_dim,
+                              float* scores, int64_t ld, hipStream_t stream) {
+  dim3 grid((unsigned)((b.max_k + 255) / 256), b.total_q);
+  indexer_f32<<<grid, 256, 0, stream>>>(q_idx, k_idx, w, b.cu_q, b.cu_k, b.nseq, b.total_q,
+                                        b.total_k, index_n_heads, index_head_dim, scores, ld);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,50 @@
+// Host-side launch interface of the libdsa kernels (one translation unit per step).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct Batch {
+  int nseq;
+  int total_q;
+  int64_t total_k;
+  int max_q;
+  int max_k;
+  const int32_t* cu_q;
+  const int64_t* cu_k;
+};
+
+// Step 1: lightning indexer. index_head_dim is 128 on the bf16 path.
+hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_idx,
+                               const float* w, int index_n_heads, float* scores, int64_t ld,
+                               hipStream_t stream);
+hipError_t launch_indexer_f32(const Batch& b, const float* q_idx, const float* k_idx,
+                              const float* w, int index_n_heads, int index_head_dim,
+                              float* scores, int64_t ld, hipStream_t stream);
+
+// Step 2: causal top-k.
+size_t topk_workspace_bytes(const Batch& b, int k);
+hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
+                       void* workspace, hipStream_t stream);
+
+// Step 3: sparse MLA (MQA) forward.
+struct MlaPlan {
+  int nsplit;
+  int rows_per_split;
+  size_t workspace;
+};
+MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads);
+hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
+                                  const int32_t* indices, int k, int n_heads, float scale,
+                                  void* out, float* lse, void* workspace, const MlaPlan& plan,
+                                  hipStream_t stream);
+hipError_t launch_sparse_mla_f32(const Batch& b, const float* q, const float* kv,
+                                 const int32_t* indices, int k, int n_heads, int d_qk, int d_v,
+                                 float scale, float* out, float* lse, hipStream_t stream);
+
+constexpr int kMaxF32TopK = 8192;  // fp32 path keeps one softmax row in LDS
+
+}  // namespace dsa

@@ -1,0 +1,402 @@
+"""GPU parity: libdsa (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bar: indexer scores and top-k indices bit-exact (integer-valued indexer inputs make every fp32
+score exact); attention outputs within max|d| <= 2e-2 and ||d||/||ref|| <= 1e-2 (tolerance.py).
+Small workloads are compared on every row; the full-size workloads on sampled rows the oracle
+computes one by one, plus properties checked on every row.
+"""
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as DI
+import long_context_lightning_amd as dsa
+import oracle.dsa_oracle as O
+from tolerance import attn_close, attn_errors
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()  # fail loudly if libdsa.so is missing
+
+
+def host64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def batch_of(case, d):
+    return dsa.Batch(d["cu_seqlens_q"], d["cu_seqlens_k"], max(case.seqlens_q),
+                     max(case.seqlens_k), case.total_q, case.total_k)
+
+
+class Row:
+    """Oracle results for one query row, computed from host copies of just what it needs."""
+
+    def __init__(self, case, d, t, layers=(0,)):
+        rows = DI.query_rows(case)
+        _, b, p, base = rows[t]
+        self.t, self.p, self.base = t, p, base
+        kI = host64(d["k_idx"][base:base + p + 1])
+        self.scores = O.indexer_scores_row(host64(d["q_idx"][t]), kI, host64(d["w"][t]))
+        self.idx = O.topk_row(self.scores, case.index_topk)
+        sel = self.idx[self.idx >= 0]
+        self.attn = {}
+        for l in layers:
+            kv_rows = host64(d["kv"][l][base + torch.as_tensor(sel, device=d["kv"][l].device)])
+            self.attn[l] = O.sparse_attention_row(host64(d["q"][l][t]), kv_rows, case.d_v,
+                                                  case.softmax_scale)
+
+
+def check_rows(case, d, scores, idx, outs, lses, sample, layers=(0,)):
+    """Bit-exact scores and indices, tolerance on outputs, for the sampled rows."""
+    got_o = {l: [] for l in layers}
+    ref_o = {l: [] for l in layers}
+    for t in sample:
+        r = Row(case, d, t, layers)
+        n = r.p + 1
+        if scores is not None:
+            gs = scores[t, :n].double().cpu().numpy()
+            bad = np.nonzero(gs != r.scores)[0]
+            assert bad.size == 0, f"row {t}: {bad.size} score mismatches, first at {bad[:5]}"
+        gi = idx[t].cpu().numpy().astype(np.int64)
+        assert np.array_equal(gi, r.idx), f"row {t}: indices differ ({np.sum(gi != r.idx)})"
+        for l in layers:
+            got_o[l].append(outs[l][t].float().cpu().numpy())
+            ref_o[l].append(r.attn[l][0])
+            if lses is not None:
+                gl = lses[l][t].double().cpu().numpy()
+                assert np.allclose(gl, r.attn[l][1], rtol=0, atol=2e-3), (t, gl[:4], r.attn[l][1][:4])
+    for l in layers:
+        ok, a, rel = attn_close(np.stack(got_o[l]), np.stack(ref_o[l]))
+        say(f"  layer {l}: max|d|={a:.3e} rel={rel:.3e} over {len(sample)} rows")
+        assert ok, (l, a, rel)
+    return got_o, ref_o
+
+
+def row_properties(case, idx):
+    """Every row: ascending, unique, within 0..p, -1 only as trailing padding, and dense when
+    p+1 <= k."""
+    rows = DI.query_rows(case)
+    k = case.index_topk
+    p = torch.tensor([r[2] for r in rows], device=idx.device, dtype=torch.int64)
+    i64 = idx.to(torch.int64)
+    n_valid = torch.clamp(p + 1, max=k)
+    pos = torch.arange(k, device=idx.device)[None, :]
+    valid = pos < n_valid[:, None]
+    assert bool(((i64 >= 0) == valid).all()), "padding not exactly where expected"
+    assert bool((i64[valid.expand_as(i64)] >= 0).all())
+    assert bool(((i64 <= p[:, None]) | ~valid).all()), "index beyond the causal position"
+    inc = (i64[:, 1:] > i64[:, :-1]) | ~valid[:, 1:]
+    assert bool(inc.all()), "not strictly ascending"
+    dense = (p + 1) <= k
+    if bool(dense.any()):
+        want = torch.where(valid, pos.expand_as(i64), torch.full_like(i64, -1))
+        assert bool((i64[dense] == want[dense]).all()), "dense rows must select 0..p"
+
+
+def run_path(case, d, batch, layer=0, lse=True):
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    idx = dsa.topk(scores, batch, case.index_topk)
+    out, l = dsa.sparse_mla_fwd(d["q"][layer], d["kv"][layer], idx, batch, case.softmax_scale,
+                                case.d_v, return_lse=lse)
+    torch.cuda.synchronize()
+    return scores, idx, out, l
+
+
+# ------------------------------------------------------------------------------ workloads
+def test_tiny_prefill_fp32_all_rows():
+    case = DI.CASES["tiny_prefill_fp32"]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    got, ref = check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+    a, _ = attn_errors(np.stack(got[0]), np.stack(ref[0]))
+    assert a < 1e-4, f"fp32 path should agree to ~1e-5, got {a}"
+
+
+def test_decode_b32_l16k_all_rows():
+    case = DI.CASES["decode_b32_l16k"]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+
+
+def test_decode_forward_matches_separate_calls():
+    case = DI.CASES["decode_b32_l16k"]
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    s1, i1, o1, l1 = run_path(case, d, batch)
+    o2, l2, i2 = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                             case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # determinism: a second run is bit-identical
+    o3, l3, i3 = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                             case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i3) and torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.slow
+def test_prefill_chunk8k_l64k_sampled():
+    case = DI.CASES["prefill_chunk8k_l64k"]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    T = case.total_q
+    sample = [0, 1, 15, 16, 17, 777, 4095, 4096, T - 17, T - 2, T - 1]
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, sample)
+
+
+@pytest.mark.slow
+def test_indexshare_b8_l256k_sampled():
+    case = DI.CASES["indexshare_b8_l256k"]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    shared = None
+    outs, lses = {}, {}
+    for l in range(case.layers):
+        o, ls, shared = dsa.forward(d["q"][l], d["kv"][l], batch, case.index_topk,
+                                    case.softmax_scale, case.d_v, q_idx=d["q_idx"],
+                                    k_idx=d["k_idx"], w=d["w"], shared_indices=shared,
+                                    compute_indices=(l == 0))
+        outs[l], lses[l] = o, ls
+    torch.cuda.synchronize()
+    row_properties(case, shared)
+    # reuse is bit-identical to running the layer on its own with the same indices
+    for l in (1, 3):
+        o, ls = dsa.sparse_mla_fwd(d["q"][l], d["kv"][l], shared, batch, case.softmax_scale,
+                                   case.d_v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, outs[l]) and torch.equal(ls, lses[l])
+    # the cached indices are what a fresh indexer + top-k produce
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    fresh = dsa.topk(scores, batch, case.index_topk)
+    torch.cuda.synchronize()
+    assert torch.equal(fresh, shared)
+    check_rows(case, d, scores, shared, outs, lses, [0, 5, 7], layers=tuple(range(4)))
+
+
+@pytest.mark.slow
+def test_mixed_b16_l512_1m_sampled():
+    case = DI.CASES["mixed_b16_l512_1m"]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    lens = list(case.seqlens_k)
+    sample = sorted({lens.index(512), lens.index(723), lens.index(1048576), lens.index(14109),
+                     lens.index(861235), lens.index(3060)})
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, sample)
+
+
+# ----------------------------------------------------------------------------- edge cases
+def _small_case(name, seqlens_k, seqlens_q, **kw):
+    return DI.custom_case(name, seqlens_k, seqlens_q,
+                          seed_base=zlib.crc32(name.encode()) % 100000 * 100, **kw)
+
+
+@pytest.mark.parametrize("lens,nq,k", [
+    ((1,), (1,), 2048),                       # single visible token
+    ((2047, 2048, 2049, 2050), (1, 1, 1, 1), 2048),   # around the dense threshold
+    ((37, 3000, 5, 9000, 65), (1, 2, 1, 3, 4), 64),   # ragged decode + multi-query rows
+    ((300, 129), (40, 17), 64),              # short prefill chunks (prefill indexer kernel)
+    ((4100,), (4100,), 2048),                # whole-sequence prefill
+])
+def test_ragged_edge_cases(lens, nq, k):
+    case = _small_case(f"edge_{lens}_{nq}_{k}", lens, nq, index_topk=k)
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    dsa.check_batch(batch)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    T = case.total_q
+    sample = range(T) if T <= 64 else sorted(set([0, 1, T // 2, T - 2, T - 1] + list(range(0, T, T // 16))))
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, sample)
+
+
+def test_index_heads_64_and_attention_heads_128():
+    case = _small_case("heads", (5000, 700), (1, 1), index_n_heads=64, n_heads=128)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+
+
+def test_all_equal_scores_take_lowest_positions():
+    case = _small_case("ties", (9000, 3000), (1, 2))
+    d = DI.make_inputs(case, "cuda")
+    d["w"].zero_()                              # every score is 0 (some -0.0 via (-x)*0)
+    d["q_idx"][:, :, ::2] *= -1
+    batch = batch_of(case, d)
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    idx = dsa.topk(scores, batch, case.index_topk)
+    torch.cuda.synchronize()
+    want = torch.arange(case.index_topk, device="cuda", dtype=torch.int32)
+    assert bool((idx == want[None, :]).all())
+
+
+def test_heavy_ties_match_oracle():
+    # w in {0, 1} and q_I in {-1, 0, 1}: scores take few values, so the k-th falls in a big tie
+    case = _small_case("heavy_ties", (20000, 40000), (1, 1), idx_range=1, w_range=1)
+    d = DI.make_inputs(case, "cuda")
+    d["w"].clamp_(min=0)
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+
+
+def test_sparse_mla_invariants():
+    case = _small_case("mla_inv", (6000, 2500, 9000), (1, 1, 1))
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    # permuting each row's selected set leaves the output unchanged (within tolerance)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    perm = torch.argsort(torch.rand(idx.shape, generator=g, device="cuda"), dim=1)
+    out_p, lse_p = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], torch.gather(idx, 1, perm).contiguous(),
+                                      batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    ok, a, r = attn_close(out_p.float().cpu().numpy(), out.float().cpu().numpy(), 1e-2, 5e-3)
+    assert ok, (a, r)
+    # V == 1 gives 1 everywhere
+    kv1 = d["kv"][0].clone()
+    kv1[:, :case.d_v] = 1
+    o1, _ = dsa.sparse_mla_fwd(d["q"][0], kv1, idx, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    assert bool((o1.float() == 1).all())
+    # -1 and out-of-range entries are skipped: masking half the row equals dropping it
+    half = idx.clone()
+    half[:, 1::2] = -1
+    oh, lh = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], half, batch, case.softmax_scale, case.d_v)
+    oor = idx.clone()
+    oor[:, 1::2] = 10 ** 8
+    oo, lo = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], oor, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(oh, oo) and torch.equal(lh, lo)
+    for t in range(case.total_q):
+        r = Row(case, d, t)
+        sel = half[t].cpu().numpy()
+        sel = sel[sel >= 0]
+        o_ref, _ = O.sparse_attention_row(host64(d["q"][0][t]),
+                                          host64(d["kv"][0][r.base + torch.as_tensor(sel, device="cuda")]),
+                                          case.d_v, case.softmax_scale)
+        ok, a, rel = attn_close(oh[t].float().cpu().numpy(), o_ref)
+        assert ok, (t, a, rel)
+    # a row with no valid index gives zeros and lse = -inf
+    none = torch.full_like(idx, -1)
+    on, ln = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], none, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    assert bool((on.float() == 0).all()) and bool(torch.isneginf(ln).all())
+
+
+def _controls(case, d, out, rows, which):
+    got = np.stack([out[r.t].float().cpu().numpy() for r in rows])
+    ok, a, rel = attn_close(got, np.stack([r.attn[0][0] for r in rows]))
+    assert ok, (a, rel)
+    res = {}
+    for name in which:
+        ref = []
+        for r in rows:
+            q = host64(d["q"][0][r.t])
+            sel = r.idx[r.idx >= 0].copy()
+            scale = case.softmax_scale
+            if name == "one_wrong_index":
+                unsel = np.setdiff1d(np.arange(r.p + 1), sel)
+                sel[len(sel) // 2] = unsel[0]
+            kvr = host64(d["kv"][0][r.base + torch.as_tensor(np.sort(sel), device="cuda")])
+            if name == "dropped_rope":
+                kvr[:, case.d_v:] = 0
+            if name == "scale_1/sqrt(512)":
+                scale = 1 / math.sqrt(512)
+            ref.append(O.sparse_attention_row(q, kvr, case.d_v, scale)[0])
+        ok, a, rel = attn_close(got, np.stack(ref))
+        say(f"  negative control {name}: max|d|={a:.3e} rel={rel:.3e}")
+        res[name] = ok
+    return res
+
+
+def test_negative_controls_decode():
+    """At the decode distribution (q, kv ~ 0.1 N(0,1), scale 1/24) the logits are nearly flat,
+    so the output is essentially the mean value row of the selected set: the bar must catch a
+    single wrong index per row."""
+    case = DI.CASES["decode_b32_l16k"]
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    rows = [Row(case, d, t) for t in range(8)]
+    res = _controls(case, d, out, rows, ["one_wrong_index"])
+    assert not any(res.values()), res
+
+
+def test_unit_variance_decode_and_controls():
+    """q, kv ~ N(0,1): logits have unit spread, so the QK product matters; parity on every row and
+    the bar must catch dropped rope columns, a wrong scale and one wrong index."""
+    case = _small_case("decode_sigma1", (16384,) * 8, (1,) * 8, sigma=1.0)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+    rows = [Row(case, d, t) for t in range(case.total_q)]
+    res = _controls(case, d, out, rows, ["one_wrong_index", "dropped_rope", "scale_1/sqrt(512)"])
+    assert not any(res.values()), res
+
+
+def _crafted_topk(rows_scores, k):
+    """Run dsa_topk on explicit score rows (one decode sequence per row) and compare with the
+    oracle's top-k row by row."""
+    lens = [len(r) for r in rows_scores]
+    batch = dsa.Batch.from_lengths([1] * len(lens), lens)
+    ld = max(lens)
+    sc = torch.zeros((len(lens), ld), dtype=torch.float32)
+    for i, r in enumerate(rows_scores):
+        sc[i, :len(r)] = torch.from_numpy(np.asarray(r, dtype=np.float32))
+    idx = dsa.topk(sc.cuda(), batch, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for i, r in enumerate(rows_scores):
+        want = O.topk_row(np.asarray(r, dtype=np.float32).astype(np.float64), k)
+        assert np.array_equal(got[i], want), (i, len(r), np.sum(got[i] != want))
+
+
+def test_topk_crafted_rows():
+    rng = np.random.default_rng(5)
+    rows = []
+    z = rng.integers(-1, 2, 50000).astype(np.float32)          # heavy ties incl. signed zeros
+    z[(z == 0) & (rng.random(50000) < 0.5)] = -0.0
+    rows.append(z)
+    rows.append(np.where(rng.random(40000) < 0.5, np.float32(0.0), np.float32(-0.0)))
+    rows.append(rng.normal(size=70000).astype(np.float32))      # longer than the LDS key cache
+    rows.append(rng.normal(size=9000).astype(np.float32) * 1e-30)   # tiny magnitudes
+    rows.append(np.concatenate([np.full(3000, 5.0), np.full(3000, -5.0)]).astype(np.float32))
+    rows.append(np.arange(20000, dtype=np.float32))             # strictly increasing
+    rows.append(-np.arange(20000, dtype=np.float32))            # strictly decreasing
+    big = rng.integers(-3, 4, 300000).astype(np.float32)        # long row, huge tie groups
+    rows.append(big)
+    rows.append(np.array([np.inf, -np.inf, 1.0, 3.0e38, -3.0e38] * 1000, dtype=np.float32))
+    _crafted_topk(rows, 2048)
+    _crafted_topk([r[:5000] for r in rows], 7)
