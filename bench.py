@@ -1,0 +1,227 @@
+"""Benchmark of the DSA decode hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch: lightning indexer -> causal top-k ->
+sparse MLA (plus the split-KV merge), on the decode workload of 32 sequences with 16384-token
+contexts, one new query each (indexer 32 heads x 128, top-k 2048, 64-head MQA over 576-wide
+bf16 latent rows). Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Steps rotate over several independent input sets whose total size exceeds the 256 MB
+Infinity Cache, so a step cannot be served from the previous step's cached lines.
+
+Prints one JSON line: metric, value (query tokens/s), per-kernel times from HIP events on the
+launch stream inside the timed region, the roofline of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b32_l16k")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def step_bytes(case):
+    """Algorithmic HBM bytes of one step: every key row of the indexer cache, the selected
+    latent rows, queries, outputs, indexer queries and weights (intermediates excluded)."""
+    import dsa_inputs as DI
+    tot = 0
+    for t, b, p, base in DI.query_rows(case):
+        n = p + 1
+        tot += n * case.index_head_dim * 2                                  # k_I rows
+        tot += min(case.index_topk, n) * case.d_qk * 2 * case.layers        # gathered rows
+        tot += case.n_heads * (case.d_qk + case.d_v) * 2 * case.layers      # q in, out
+        tot += case.index_n_heads * (case.index_head_dim * 2 + 4)           # q_I, w
+    return tot
+
+
+def indexer_bytes(case):
+    import dsa_inputs as DI
+    tot = 0
+    for t, b, p, base in DI.query_rows(case):
+        tot += (p + 1) * case.index_head_dim * 2 + case.index_n_heads * (case.index_head_dim * 2 + 4)
+    return tot
+
+
+def mla_bytes(case):
+    import dsa_inputs as DI
+    tot = 0
+    for t, b, p, base in DI.query_rows(case):
+        tot += min(case.index_topk, p + 1) * case.d_qk * 2 + case.n_heads * (case.d_qk + case.d_v) * 2
+    return tot
+
+
+def cpu_baseline(case, sets, budget_s):
+    """The oracle as it stands, on a bounded sample of decode queries (host copies made before
+    each timed query)."""
+    import numpy as np
+    import torch
+    import dsa_inputs as DI
+    import oracle.dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+
+    rows = DI.query_rows(case)
+    d = sets[0]
+    host = []                     # host copies (float32) of what each sampled query reads
+    for t, b, p, base in rows[:32]:
+        f = lambda x: x.detach().float().cpu().numpy()
+        host.append((f(d["q_idx"][t]), f(d["k_idx"][base:base + p + 1]), f(d["w"][t]),
+                     f(d["q"][0][t]), f(d["kv"][0][base:base + p + 1])))
+    done, spent = 0, 0.0
+    while spent < budget_s and done < 100000:
+        qI, kI, w, q, kv = host[done % len(host)]
+        t0 = time.perf_counter()
+        s = O.indexer_scores_row(qI, kI, w)
+        sel = O.topk_row(s, case.index_topk)
+        O.sparse_attention_row(q, kv[sel[sel >= 0]], case.d_v, case.softmax_scale)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": done / spent, "unit": "query-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} decode queries of the same workload (full indexer over "
+                      f"{max(case.seqlens_k)} keys, top-{case.index_topk}, {case.n_heads}-head "
+                      f"sparse attention; {len(host)} distinct queries cycled), float64 NumPy, "
+                      f"{spent:.1f} s of oracle time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the DSA path on one GPU only; --gpus {args.gpus} is "
+              "not supported (decode shards by sequence, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dsa_inputs as DI
+    import long_context_lightning_amd as dsa
+
+    torch.cuda.set_device(0)
+    case = DI.CASES[args.workload]
+    set_bytes = (case.total_k * (case.index_head_dim + case.d_qk * case.layers) * 2)
+    nsets = args.sets or max(2, math.ceil((1 << 30) / set_bytes))
+    sets = []
+    for i in range(nsets):
+        c = DI.Case(**{**case.__dict__, "seed_base": case.seed_base + 100 * i})
+        sets.append(DI.make_inputs(c, "cuda"))
+    d0 = sets[0]
+    batch = dsa.Batch(d0["cu_seqlens_q"], d0["cu_seqlens_k"], max(case.seqlens_q),
+                      max(case.seqlens_k), case.total_q, case.total_k)
+    T = case.total_q
+    ld = batch.max_seqlen_k
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, case.index_topk), dtype=torch.int32, device="cuda")
+    outs = [torch.empty((T, case.n_heads, case.d_v), dtype=case.dtype, device="cuda")
+            for _ in range(case.layers)]
+    lse = torch.empty((T, case.n_heads), dtype=torch.float32, device="cuda")
+    ws_n = dsa.workspace_size(dsa.OP_SPARSE_MLA, batch, case.index_topk, case.n_heads, case.d_v)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    L = dsa.lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, ev=None):
+        d = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        st = L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
+                                  d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
+                                  1, scores.data_ptr(), ld, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
+                         None, 0, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        for l in range(case.layers):       # IndexShare: the group's layers reuse the indices
+            st |= L.dsa_sparse_mla_fwd(batch.ptr, d["q"][l].data_ptr(), d["kv"][l].data_ptr(),
+                                       idx.data_ptr(), case.index_topk, case.n_heads, case.d_qk,
+                                       case.d_v, case.softmax_scale, 1, outs[l].data_ptr(),
+                                       lse.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        if ev is not None:
+            ev[3].record(stream)
+        if st:
+            raise RuntimeError(f"libdsa call failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_idx = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_topk = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_mla = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    ms_gpu = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    sb = step_bytes(case)
+    ib, mb = indexer_bytes(case), mla_bytes(case) // case.layers
+    kern = {"indexer": (ms_idx, ib), "sparse_mla": (ms_mla / case.layers, mb)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dms, dbytes = kern[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": dbytes,
+            "avg_launch_ms": round(dms, 5)}
+    line = {
+        "metric": "DSA decode query-tokens/s + achieved HBM GB/s (indexer+top-k+sparse MLA)",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.dtype.__str__().endswith("bfloat16") else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name}: {case.batch} sequences, contexts "
+                               f"{min(case.seqlens_k)}..{max(case.seqlens_k)}, "
+                               f"{case.total_q} query tokens, indexer {case.index_n_heads}x"
+                               f"{case.index_head_dim}, top-{case.index_topk}, "
+                               f"{case.n_heads}-head MQA over {case.d_qk}-wide latent "
+                               f"({case.d_v} value), {case.layers} layer(s) per index pass",
+                   "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets},
+        "achieved_hbm_gbps": round(sb / (ms_step * 1e-3) / 1e9, 1),
+        "algorithmic_bytes_per_step": sb,
+        "kernel_ms": {"indexer": round(ms_idx, 5), "topk": round(ms_topk, 5),
+                      "sparse_mla_incl_merge": round(ms_mla, 5), "gpu_step": round(ms_gpu, 5)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, sets, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
