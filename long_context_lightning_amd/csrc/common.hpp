@@ -100,6 +100,20 @@ __device__ __forceinline__ int find_seq(const I* __restrict__ cu, int nseq, int6
   return lo;
 }
 
+// Same result as find_seq, computed by a whole wave (all 64 lanes must call it with the same x):
+// 64 entries are compared per load and the ascending prefix is counted with a ballot, so the
+// lookup costs one memory latency per 64 sequences instead of one per bisection step.
+template <typename I>
+__device__ __forceinline__ int find_seq_wave(const I* __restrict__ cu, int nseq, int64_t x) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  for (int base = 0;; base += WAVE) {
+    const int i = base + 1 + lane;
+    const bool le = i < nseq && (int64_t)cu[i] <= x;
+    const int cnt = __popcll(__ballot(le));
+    if (cnt < WAVE) return base + cnt;
+  }
+}
+
 // Position of query row t: sequence b, position p (may see 0..p), key base and length.
 struct QueryPos {
   int b;
@@ -108,11 +122,12 @@ struct QueryPos {
   int64_t len;      // L_b
 };
 
+// t must be the same for all 64 lanes of the wave (the lookup is a wave-wide ballot).
 __device__ __forceinline__ QueryPos query_pos(const int32_t* __restrict__ cu_q,
                                               const int64_t* __restrict__ cu_k, int nseq,
                                               int64_t total_k, int t) {
   QueryPos r;
-  r.b = find_seq(cu_q, nseq, t);
+  r.b = find_seq_wave(cu_q, nseq, t);
   int64_t q0 = cu_q[r.b], q1 = cu_q[r.b + 1];
   int64_t k0 = cu_k[r.b], k1 = cu_k[r.b + 1];
   k0 = max((int64_t)0, min(k0, total_k));

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK + (int64_t)wave * DEC_KEYS_PER_WAVE;
   const int64_t f_end = min(f + DEC_KEYS_PER_WAVE, total_k);
   while (f < f_end) {
-    const int b = find_seq(cu_k, nseq, f);
+    const int b = find_seq_wave(cu_k, nseq, f);
     const int64_t kb0 = cu_k[b];
     const int64_t kb1 = min(cu_k[b + 1], total_k);
     if (kb1 <= f || kb0 > f) break;

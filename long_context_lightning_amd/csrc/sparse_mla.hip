@@ -7,8 +7,8 @@
 // bf16 kernel: one workgroup = (query, KV split, group of 64 heads), 4 waves.
 //   * Tiles of 64 selected rows are gathered straight from HBM into LDS with direct
 //     global->LDS 16-byte loads (double-buffered: tile i+1 streams in while tile i computes).
-//     Each row's 72 chunks of 16 B are stored with the chunk slot XOR-ed by (row & 7) so the
-//     MFMA operand reads of 32 consecutive rows hit distinct LDS banks.
+//     Each row's 72 chunks of 16 B are stored with the chunk slot XOR-ed by a 3-bit function
+//     of the row (swz) that keeps every MFMA operand read free of LDS bank conflicts.
 //   * QK^T is computed transposed, S^T[rows x heads] = KV[rows x 576] * Q^T, on 32x32x16 MFMAs:
 //     wave w owns rows 32*(w&1).. and heads 32*(w>>1)..; the query block is resident in
 //     registers (B operand) and KV rows are the A operand read from LDS. In this layout each
@@ -35,117 +35,227 @@ constexpr int TILE = 64;                     // selected rows per LDS stage
 constexpr int ROWB = DQK * 2;                // 1152 bytes per latent row
 constexpr int CHUNKS = ROWB / 16;            // 72 chunks of 16 B
 constexpr int STAGE_BYTES = TILE * ROWB;     // 73728
+constexpr int ROPE_OFF = DV * 2;             // byte offset of the RoPE columns in a row
 constexpr int P_STRIDE = TILE + 8;           // bf16 elements per head row of P (padded)
-constexpr int OFF_P = 2 * STAGE_BYTES;
-constexpr int OFF_XMAX = OFF_P + HG * P_STRIDE * 2;
-constexpr int OFF_XSUM = OFF_XMAX + 2 * HG * 4;
-constexpr int OFF_ALPHA = OFF_XSUM + 2 * HG * 4;
-constexpr int MLA_LDS = OFF_ALPHA + HG * 4;
+constexpr int OFF_R = 2 * STAGE_BYTES;       // 16 KB: QK half-sum exchange, then P
+constexpr int R_BYTES = 16384;
+constexpr int MLA_LDS = OFF_R + R_BYTES;     // 160 KB
 constexpr int LOADS_PER_THREAD = STAGE_BYTES / 16 / 256;   // 18
+constexpr int QK_STEPS = DQK / 16 / 2;       // 18 MFMA k-steps per K half
 static_assert(LOADS_PER_THREAD * 256 * 16 == STAGE_BYTES, "stage must split evenly");
+static_assert(HG * P_STRIDE * 2 <= R_BYTES && 4 * 16 * 64 * 4 == R_BYTES, "R region");
 static_assert(MLA_LDS <= 160 * 1024, "LDS budget");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kHeadroom = 16.f;            // log2 headroom of a reference maximum
+
+// LDS slot of 16-byte chunk c of tile row r is c ^ swz(r). swz takes all 8 values on every 8
+// aligned rows and distinct values on the even and on the odd rows of every 16, so the QK
+// operand reads (32 consecutive rows, one chunk) are conflict-free for 32- and 64-bank LDS;
+// and within every aligned 4-row block its bits (2,1) take all four values with bit 2 differing
+// between rows r and r+2, which makes the transposed V reads (4 rows x 64 bytes) conflict-free.
+// The RoPE chunks 64..71 stay in slots 64..71 (the XOR only touches the low 3 bits).
+__device__ __forceinline__ int swz(int r) {
+  return (2 * (r & 3) + ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1);
+}
 
 // Hides a value from loop-invariant code motion so per-tile address math is recomputed
 // instead of occupying registers across the tile loop.
 __device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
 
+// s_waitcnt vmcnt(N) with the other counters left alone (GFX9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Softmax statistics live in the RoPE columns of the tile being processed: those columns are
+// only read by QK^T, which every wave has finished before the first statistic is written.
+// Float i sits in row i/32 at RoPE byte 4*(i%32).
+__device__ __forceinline__ float* stat(char* stage, int i) {
+  return (float*)(stage + (i >> 5) * ROWB + ROPE_OFF + (i & 31) * 4);
+}
+constexpr int ST_MAX = 0;       // [2][HG] per row-block tile maximum
+constexpr int ST_SUM = 128;     // [2][HG] per row-block tile sum
+constexpr int ST_FLAG = 256;    // [4]     wave saw a tile beyond its reference headroom
+
+// grid: 1-D, 8 * ceil(T/8) * nsplit * (H/64) workgroups. Consecutive workgroups are dispatched
+// round-robin to the 8 XCDs; the mapping below gives all splits of one query the same XCD so
+// its query block is fetched into that XCD's L2 once.
 __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ indices, int k, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int H,
-    float scale_log2, int nsplit, int rows_per_split, __bf16* __restrict__ out,
+    float scale_log2, int nsplit, int rows_per_split, int tgroups, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int split = blockIdx.x;
-  const int t = blockIdx.y;
-  const int hg = blockIdx.z;
+  const int xcd = blockIdx.x & 7;
+  const int kk = blockIdx.x >> 3;
+  const int split = kk % nsplit;
+  const int rest = kk / nsplit;
+  const int t = (rest % tgroups) * 8 + xcd;
+  const int hg = rest / tgroups;
+  if (t >= total_q) return;
+
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c32 = lane & 31;
-  const int rb = wave & 1;        // QK: row block of the tile
+  const int kh = wave & 1;        // QK: K half (columns 288*kh ..)
   const int hb = wave >> 1;       // QK and PV: head block within the group
+  const int rb = kh;              // after the half-sum exchange: row block owned
   const int dvh = wave & 1;       // PV: value-column half
   const int head_lane = hb * 32 + c32;   // head (within the group) of this lane's softmax stats
 
   const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, t);
   const int64_t L = qp.len;
+  const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
   const int r_beg = split * rows_per_split;
   const int r_end = min(k, r_beg + rows_per_split);
   const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const int32_t* irow = indices + (int64_t)t * k;
   const __bf16* kvb = kv + qp.key_base * DQK;
+  __bf16* pl = (__bf16*)(lds + OFF_R);        // [HG][P_STRIDE]
+  float* xch = (float*)(lds + OFF_R);         // [4 waves][16][64]
 
-  float* xmax = (float*)(lds + OFF_XMAX);     // [2][HG]
-  float* xsum = (float*)(lds + OFF_XSUM);     // [2][HG]
-  float* xalpha = (float*)(lds + OFF_ALPHA);  // [HG]
-  __bf16* pl = (__bf16*)(lds + OFF_P);        // [HG][P_STRIDE]
-
+  // Softmax with a fixed reference maximum per head: the first tile in which a head has a finite
+  // logit sets its reference m_ref, and probabilities are exp2(s - m_ref) without rescaling the
+  // output block. If a later tile exceeds a reference by more than 2^kHeadroom, the workgroup
+  // raises the references and restarts its split (softmax is shift-invariant, so the result is
+  // the same). This keeps every update of the output accumulators inside the MFMA pipe.
   f32x16 o[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   if (ntiles > 0) {
-    bf16x8 qreg[36];
-    {
-      const __bf16* qr = q + ((int64_t)t * H + hg * HG + head_lane) * DQK + half * 8;
-#pragma unroll
-      for (int st = 0; st < 36; ++st) qreg[st] = *(const bf16x8*)(qr + st * 16);
-    }
+    // index of tile row `lane`; always issues one load so the vmcnt bookkeeping is uniform
     auto load_idx = [&](int tile) -> int {
       const int r = r_beg + tile * TILE + lane;
-      return (tile < ntiles && r < r_end) ? irow[r] : -1;
+      const int v = irow[min(r, k - 1)];
+      return (tile < ntiles && r < r_end) ? v : -1;
     };
+    // gathers one tile: slot c*256+tid of the stage holds chunk (slot%72)^swz(row) of row
+    // slot/72; always issues LOADS_PER_THREAD loads (invalid rows read row 0, masked later)
     auto issue = [&](int idxv, int stg) {
       char* base = lds + stg * STAGE_BYTES;
-      int slot = tid;
-      opaque(slot);                          // recomputed per tile instead of held in registers
+      int tt = tid;
+      opaque(tt);                            // recomputed per tile instead of held in registers
 #pragma unroll
-      for (int c = 0; c < LOADS_PER_THREAD; ++c, slot += 256) {
-        const int row = slot / CHUNKS;
-        const int gc = (slot - row * CHUNKS) ^ (row & 7);
-        const int v = __shfl(idxv, row, WAVE);
-        const int64_t r = (v >= 0 && v < L) ? v : 0;
-        global_to_lds16(kvb + r * DQK + gc * 8, base + (c * 256 + wave * 64) * 16);
+      for (int g = 0; g < LOADS_PER_THREAD / 6; ++g) {
+        int vs[6], gcs[6];
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+          const int slot = (g * 6 + j) * 256 + tt;
+          const int row = slot / CHUNKS;
+          gcs[j] = (slot - row * CHUNKS) ^ swz(row);
+          vs[j] = __shfl(idxv, row, WAVE);
+        }
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+          const uint32_t v = (uint32_t)vs[j] < Lu ? (uint32_t)vs[j] : 0u;
+          global_to_lds16(kvb + (size_t)v * DQK + gcs[j] * 8,
+                          base + ((g * 6 + j) * 256 + wave * 64) * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the groups apart: bounded live registers
       }
     };
 
-    int idx_cur = load_idx(0);
-    issue(idx_cur, 0);
-    int idx_next = load_idx(1);
+    const int idx0 = load_idx(0);
+    const int idx1 = load_idx(1);
+    issue(idx0, 0);                          // tile 0 in flight before the query block loads
+    bf16x8 qreg[QK_STEPS];
+    {
+      const __bf16* qr = q + ((int64_t)t * H + hg * HG + head_lane) * DQK +
+                         kh * (QK_STEPS * 16) + half * 8;
+#pragma unroll
+      for (int i = 0; i < QK_STEPS; ++i) qreg[i] = *(const bf16x8*)(qr + i * 16);
+    }
+    // A-operand lane bases: step i of this wave reads chunk 36*kh + 2*i + half of rows c32 and
+    // 32 + c32 (same swizzle); with u = 2*kh + i the slot is
+    // 8*(4*kh + u/4) + ((2*(u%4) + half) ^ swz): four lane bases plus 128*(i/4) immediates.
+    const int sw = swz(c32);
+    int abase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = 2 * kh + j;
+      abase[j] = c32 * ROWB + 128 * (4 * kh + (u >> 2)) + (((2 * (u & 3) + half) ^ sw) << 4);
+    }
+
+    // zeroes the output block with MFMAs (0 x 0 + 0) so every definition of o stays in the
+    // matrix-core register class
+    auto zero_o = [&]() {
+      const bf16x8 z = {};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
+    };
+    zero_o();
+    issue(idx1, 1);                          // tiles 0 and 1 in flight before the loop
+    int idx_cur = idx1;                      // indices of the newest issued tile
+    int idx_next = load_idx(2);
 
     for (int tile = 0; tile < ntiles; ++tile) {
       const int stg = tile & 1;
-      wait_all_memory();
+      if (tile == 0) wait_vmcnt<LOADS_PER_THREAD + 1>();   // tile 1 and idx 2 may be in flight
+      else wait_vmcnt<1>();                                // the next index load may be in flight
       __syncthreads();                       // tile rows landed; previous tile fully consumed
-      const int idx_tile = idx_cur;
-      if (tile + 1 < ntiles) issue(idx_next, stg ^ 1);
-      idx_cur = idx_next;
-      idx_next = load_idx(tile + 2);
-      const char* sbase = lds + stg * STAGE_BYTES;
-      const uint64_t vmask = __ballot(r_beg + tile * TILE + lane < r_end && idx_tile >= 0 &&
-                                      idx_tile < L);
+      const int idx_tile = tile == 0 ? idx0 : (tile == 1 ? idx1 : idx_cur);
+      // The next tile's gathers go out one per QK step (below) so the wave never stalls on a
+      // burst of 18 loads; their row indices are fetched from the index register first.
+      const bool do_issue = tile >= 1 && tile + 1 < ntiles;
+      int tt = tid;
+      opaque(tt);
+      int nv[LOADS_PER_THREAD];
+      if (do_issue) {
+#pragma unroll
+        for (int c = 0; c < LOADS_PER_THREAD; ++c)
+          nv[c] = __shfl(idx_next, (c * 256 + tt) / CHUNKS, WAVE);
+      }
+      char* nbase = lds + (stg ^ 1) * STAGE_BYTES;
+      auto issue_one = [&](int c) {
+        const int slot = c * 256 + tt;
+        const int row = slot / CHUNKS;
+        const int gc = (slot - row * CHUNKS) ^ swz(row);
+        const uint32_t v = (uint32_t)nv[c] < Lu ? (uint32_t)nv[c] : 0u;
+        global_to_lds16(kvb + (size_t)v * DQK + gc * 8, nbase + (c * 256 + wave * 64) * 16);
+      };
+      char* sbase = lds + stg * STAGE_BYTES;
+      const uint64_t vmask =
+          __ballot(r_beg + tile * TILE + lane < r_end && (uint32_t)idx_tile < Lu);
 
-      // ---- S^T[32 rows x 32 heads] over the full 576-wide row. Chunk 2*st+half of row arow
-      // sits in slot 8*(st/4) + ((2*(st%4)+half) ^ (arow&7)): four lane bases + immediates.
-      f32x16 s = {};
+      // ---- QK^T half sums: S^T[64 rows x 32 heads] over this wave's 288 columns
+      f32x16 s0 = {}, s1 = {};
       {
-        const int arow = rb * 32 + c32;
-        const char* abase[4];
+        bf16x8 a0[2], a1[2];
+        auto rd = [&](int i, int b) {
+          const char* pa = sbase + abase[i & 3] + (i >> 2) * 128;
+          a0[b] = *(const bf16x8*)pa;
+          a1[b] = *(const bf16x8*)(pa + 32 * ROWB);
+        };
+        static_assert(QK_STEPS == LOADS_PER_THREAD, "one gather per QK step");
+        rd(0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          abase[j] = sbase + arow * ROWB + (((2 * j + half) ^ (arow & 7)) << 4);
-#pragma unroll
-        for (int st = 0; st < 36; ++st) {
-          const bf16x8 a = *(const bf16x8*)(abase[st & 3] + (st >> 2) * 128);
-          s = mfma32x32x16(a, qreg[st], s);
+        for (int i = 0; i < QK_STEPS; ++i) {
+          if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
+          if (do_issue) issue_one(i);
+          s0 = mfma32x32x16(a0[i & 1], qreg[i], s0);
+          s1 = mfma32x32x16(a1[i & 1], qreg[i], s1);
         }
       }
+      if (tile >= 1) {
+        if (do_issue) idx_cur = idx_next;
+        idx_next = load_idx(tile + 2);
+      }
+      // ---- exchange half sums: keep row block kh, hand the other to the partner wave
+      const f32x16 give = kh ? s0 : s1;
+      f32x16 s = kh ? s1 : s0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = give[r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
+
       float sv[16];
       float mx = -INFINITY;
 #pragma unroll
@@ -155,19 +265,21 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
         mx = fmaxf(mx, sv[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      if (half == 0) xmax[rb * HG + head_lane] = mx;
+      if (half == 0) *stat(sbase, ST_MAX + rb * HG + head_lane) = mx;
       __syncthreads();
-      const float m_tile = fmaxf(xmax[head_lane], xmax[HG + head_lane]);
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      const float m_tile =
+          fmaxf(*stat(sbase, ST_MAX + head_lane), *stat(sbase, ST_MAX + HG + head_lane));
+      const bool exceed = m_ref != -INFINITY && m_tile > m_ref + kHeadroom;
+      if (m_ref == -INFINITY || exceed) m_ref = m_tile;
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       float ls = 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(sv[4 * g + e] - m_use);
+          // raw v_exp_f32: arguments are <= headroom; results below 2^-126 flush to 0
+          const float p = __builtin_amdgcn_exp2f(sv[4 * g + e] - m_use);
           ls += p;
           pk[e] = (__bf16)p;
         }
@@ -175,55 +287,78 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
         *(bf16x4*)(pl + head_lane * P_STRIDE + row0) = pk;
       }
       ls += __shfl_xor(ls, 32, WAVE);
-      if (half == 0) xsum[rb * HG + head_lane] = ls;
-      if (rb == 0 && half == 0) xalpha[head_lane] = alpha;
+      if (half == 0) *stat(sbase, ST_SUM + rb * HG + head_lane) = ls;
+      const bool wave_exceeds = __ballot(exceed) != 0;   // ballot with every lane active
+      if (lane == 0) *stat(sbase, ST_FLAG + wave) = wave_exceeds ? 1.f : 0.f;
       __syncthreads();
-      l_run = alpha * l_run + xsum[head_lane] + xsum[HG + head_lane];
-      m_run = m_new;
-
-      // ---- O[32 heads x 256 cols] = alpha * O + P[32 heads x 64 rows] * V[64 rows x 256 cols]
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float al = xalpha[hb * 32 + mfma32_row(r, lane)];
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][r] *= al;
+      const bool restart = (*stat(sbase, ST_FLAG + 0) + *stat(sbase, ST_FLAG + 1) +
+                            *stat(sbase, ST_FLAG + 2) + *stat(sbase, ST_FLAG + 3)) != 0.f;
+      if (restart) {                       // uniform across the workgroup: redo the split
+        wait_all_memory();                 // drain this pass's gathers before reusing stages
+        __syncthreads();
+        zero_o();
+        l_run = 0.f;
+        issue(idx0, 0);
+        issue(idx1, 1);
+        idx_cur = idx1;
+        idx_next = load_idx(2);
+        tile = -1;
+        continue;
       }
-      // V[krow][col] for the B operand of value block db, rows 4*rr.. of the lane's k-group:
-      // krow & 7 = j16 >> 2 and the chunk of col is 4*(8*dvh + db) + c2, so the swizzled slot is
-      // 4*((8*dvh + db) ^ rr) + (c2 ^ (j16 >> 2)): one lane base plus immediate offsets.
+      l_run += *stat(sbase, ST_SUM + head_lane) + *stat(sbase, ST_SUM + HG + head_lane);
+
+      // ---- O[32 heads x 256 cols] += P[32 heads x 64 rows] * V[64 rows x 256 cols]
+      // V[krow][col] for the B operand of value block db (32 columns), rows 4*rr.. of the
+      // lane's k-group: krow = 16*ks + rw0 + 4*rr with rw0 = 8*(g16/2) + j16/4, and chunk(col)
+      // = 4*blk + c2 with blk = 8*dvh + db. swz(rw0 + 4) = swz(rw0) ^ 1 and both share bit 2
+      // (b2), so slot = 4*(blk ^ b2) + (c2 ^ (swz & 3)): per (rr, parity of blk) one lane
+      // base, the rest immediate offsets.
       const int g16 = lane >> 4;
       const int j16 = lane & 15;
       const int c2 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-      const char* vbase = sbase + (8 * (g16 >> 1) + (j16 >> 2)) * ROWB +
-                          ((c2 ^ (j16 >> 2)) << 4) + (j16 & 1) * 8;
+      const int rw0 = 8 * (g16 >> 1) + (j16 >> 2);
+      const int sw0 = swz(rw0);
+      const int b2 = sw0 >> 2;
+      const char* vb[2][2];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const char* p = sbase + (rw0 + 4 * rr) * ROWB + ((c2 ^ ((sw0 ^ rr) & 3)) << 4) +
+                        (j16 & 1) * 8;
+        vb[rr][0] = p + 64 * b2;     // even blk: blk ^ b2 = blk + b2
+        vb[rr][1] = p - 64 * b2;     // odd blk:  blk ^ b2 = blk - b2
+      }
       const __bf16* pbase = pl + head_lane * P_STRIDE + half * 8;
 #pragma unroll
       for (int ks = 0; ks < TILE / 16; ++ks) {
         const bf16x8 pa = *(const bf16x8*)(pbase + ks * 16);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const int blk0 = 8 * dvh + db;
-          const i16x4 v0 = lds_read_tr16(vbase + ks * 16 * ROWB + (blk0 << 6));
-          const i16x4 v1 = lds_read_tr16(vbase + ks * 16 * ROWB + 4 * ROWB + ((blk0 ^ 1) << 6));
-          const bf16x8 bop = concat_bf16(v0, v1);
-          o[db] = mfma32x32x16(pa, bop, o[db]);
+          const int blk = 8 * dvh + db;
+          const i16x4 v0 = lds_read_tr16(vb[0][db & 1] + ks * 16 * ROWB + (blk << 6));
+          const i16x4 v1 = lds_read_tr16(vb[1][db & 1] + ks * 16 * ROWB + (blk << 6));
+          o[db] = mfma32x32x16(pa, concat_bf16(v0, v1), o[db]);
         }
       }
     }
+  } else {
+    const bf16x8 z = {};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
   }
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
+  float* fin = (float*)(lds + OFF_R);          // [0,64): l per head, [64,128): max per head
   __syncthreads();
-  if (rb == 0 && half == 0) {
-    xsum[head_lane] = l_run;
-    xmax[head_lane] = m_run;
+  if (kh == 0 && half == 0) {
+    fin[head_lane] = l_run;
+    fin[HG + head_lane] = m_ref;
   }
   __syncthreads();
   const int head_base = hg * HG + hb * 32;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int hl = hb * 32 + mfma32_row(r, lane);
-    const float l = xsum[hl];
+    const float l = fin[hl];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t h = head_base + mfma32_row(r, lane);
 #pragma unroll
@@ -236,9 +371,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
         part_o[(((int64_t)t * nsplit + split) * H + h) * DV + col] = v;
     }
   }
-  if (rb == 0 && dvh == 0 && half == 0) {
-    const float l = xsum[head_lane];
-    const float val = l > 0.f ? (xmax[head_lane] + log2f(l)) * kLn2 : -INFINITY;
+  if (kh == 0 && dvh == 0 && half == 0) {
+    const float l = fin[head_lane];
+    const float val = l > 0.f ? (fin[HG + head_lane] + log2f(l)) * kLn2 : -INFINITY;
     const int64_t h = hg * HG + head_lane;
     if (nsplit == 1) {
       if (lse) lse[(int64_t)t * H + h] = val;
@@ -371,11 +506,12 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
     part_o = (float*)workspace;
     part_lse = part_o + (size_t)b.total_q * plan.nsplit * n_heads * DV;
   }
-  dim3 grid(plan.nsplit, b.total_q, n_heads / HG);
-  sparse_mla_bf16<<<grid, 256, MLA_LDS, stream>>>(
+  const int tgroups = (b.total_q + 7) / 8;
+  const int64_t nblocks = (int64_t)8 * tgroups * plan.nsplit * (n_heads / HG);
+  sparse_mla_bf16<<<dim3((unsigned)nblocks), 256, MLA_LDS, stream>>>(
       (const __bf16*)q, (const __bf16*)kv, indices, k, b.cu_q, b.cu_k, b.nseq, b.total_q,
-      b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, (__bf16*)out, lse,
-      part_o, part_lse);
+      b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, tgroups,
+      (__bf16*)out, lse, part_o, part_lse);
   e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
   mla_combine<<<dim3(b.total_q, n_heads), 128, 0, stream>>>(part_o, part_lse, plan.nsplit,

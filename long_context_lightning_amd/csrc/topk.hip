@@ -8,9 +8,9 @@
 //   1. every score becomes an order-preserving 32-bit key (kept in LDS when the row fits);
 //      the row's minimum and maximum keys are reduced;
 //   2. the threshold key K* (the k-th largest) is found by repeatedly histogramming the keys
-//      that fall in the current key interval [lo, hi] into 2048 equal-width bins (exact integer
-//      bin edges) and keeping the bin that holds the k-th largest; each round divides the
-//      interval width by 2048, so at most 3 rounds reach a single key. `need` tracks how many
+//      that fall in the current key interval [lo, hi] into at most 2048 bins of a power-of-two
+//      width aligned to lo, and keeping the bin that holds the k-th largest; each round shrinks
+//      the interval at least 1024-fold, so at most 3 rounds reach a single key. `need` tracks how many
 //      keys equal to K* belong to the selection;
 //   3. compaction in index order: each thread owns a contiguous run of positions; a block scan
 //      of (count > K*, count == K*) gives every thread its output offset and the number of
@@ -62,6 +62,35 @@ __device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t& 
   __syncthreads();
 }
 
+// Calls f(i, key_i) for every position i < n of the row, each thread on positions i == tid
+// (mod TK_THREADS) in groups of four. Keys come from the LDS cache when `cached`, otherwise from
+// the fp32 scores in global memory with 16-byte loads, unrolled so several loads are in flight.
+template <typename F>
+__device__ __forceinline__ void scan_row(const float* __restrict__ srow, const uint32_t* keys,
+                                         bool cached, int64_t n, F f) {
+  const int tid = threadIdx.x;
+  const bool vec = cached || ((reinterpret_cast<uintptr_t>(srow) & 15) == 0);
+  const int64_t n4 = vec ? (n >> 2) : 0;
+  if (cached) {
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
+#pragma unroll 4
+    for (int64_t j = tid; j < n4; j += TK_THREADS) {
+      const u32x4 v = k4[j];
+      f(4 * j, v[0]); f(4 * j + 1, v[1]); f(4 * j + 2, v[2]); f(4 * j + 3, v[3]);
+    }
+  } else {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(srow);
+#pragma unroll 4
+    for (int64_t j = tid; j < n4; j += TK_THREADS) {
+      const f32x4 v = s4[j];
+      f(4 * j, score_key(v[0])); f(4 * j + 1, score_key(v[1]));
+      f(4 * j + 2, score_key(v[2])); f(4 * j + 3, score_key(v[3]));
+    }
+  }
+  for (int64_t i = 4 * n4 + tid; i < n; i += TK_THREADS)
+    f(i, cached ? keys[i] : score_key(srow[i]));
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int k,
@@ -86,12 +115,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 
   // 1. keys, minimum and maximum
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int64_t i = tid; i < n; i += TK_THREADS) {
-    const uint32_t kk = score_key(srow[i]);
+  scan_row(srow, keys, false, n, [&](int64_t i, uint32_t kk) {
     if (cached) keys[i] = kk;
     kmin = min(kmin, kk);
     kmax = max(kmax, kk);
-  }
+  });
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) { sh.red_a[wave] = kmin; sh.red_b[wave] = kmax; }
@@ -103,18 +131,20 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   __syncthreads();
   auto key_at = [&](int64_t i) -> uint32_t { return cached ? keys[i] : score_key(srow[i]); };
 
-  // 2. threshold key
+  // 2. threshold key. Bins are 2^shift keys wide, aligned to lo, with the smallest shift that
+  // fits [lo, hi] into TK_BINS bins: the bin of a key is one shift and its edges are exact.
   uint64_t lo = kmin, hi = kmax;
   uint32_t need = (uint32_t)k;                   // keys to take from [lo, hi]
   while (lo < hi) {
-    const uint64_t range = hi - lo + 1;
+    const uint64_t span = hi - lo;               // >= 1
+    int shift = 0;
+    while ((span >> shift) >= TK_BINS) ++shift;
     for (int i = tid; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += TK_THREADS) {
-      const uint32_t kk = key_at(i);
-      if (kk >= lo && kk <= hi)
-        atomicAdd(&sh.hist[(uint32_t)(((uint64_t)(kk - lo) * TK_BINS) / range)], 1u);
-    }
+    const uint32_t lo32 = (uint32_t)lo, hi32 = (uint32_t)hi;
+    scan_row(srow, keys, cached, n, [&](int64_t, uint32_t kk) {
+      if (kk >= lo32 && kk <= hi32) atomicAdd(&sh.hist[(kk - lo32) >> shift], 1u);
+    });
     __syncthreads();
     const uint32_t h0 = sh.hist[2 * tid], h1 = sh.hist[2 * tid + 1];
     uint32_t incl = h0 + h1, dummy = 0, total = 0, dtot = 0;
@@ -130,30 +160,44 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     __syncthreads();
     const uint64_t bin = sh.sel_bin;
     need = sh.sel_need;
-    const uint64_t nlo = lo + (bin * range + TK_BINS - 1) / TK_BINS;
-    const uint64_t nhi = lo + ((bin + 1) * range + TK_BINS - 1) / TK_BINS - 1;
-    lo = nlo;
-    hi = nhi;
+    lo = lo + (bin << shift);
+    hi = min(hi, lo + (((uint64_t)1 << shift) - 1));
     __syncthreads();
   }
   const uint32_t kstar = (uint32_t)lo;
 
   // 3. compaction in index order
-  const int64_t per = (n + TK_THREADS - 1) / TK_THREADS;
+  const int64_t per = ((n + TK_THREADS - 1) / TK_THREADS + 3) & ~(int64_t)3;
   const int64_t i0 = min((int64_t)tid * per, n);
   const int64_t i1 = min(i0 + per, n);
+  const bool vec = cached || ((reinterpret_cast<uintptr_t>(srow) & 15) == 0);
+  auto run = [&](auto&& f) {                     // f(i, key) over this thread's run, in order
+    int64_t i = i0;
+    if (vec) {
+#pragma unroll 4
+      for (; i + 4 <= i1; i += 4) {
+        if (cached) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(keys + i);
+          f(i, v[0]); f(i + 1, v[1]); f(i + 2, v[2]); f(i + 3, v[3]);
+        } else {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(srow + i);
+          f(i, score_key(v[0])); f(i + 1, score_key(v[1]));
+          f(i + 2, score_key(v[2])); f(i + 3, score_key(v[3]));
+        }
+      }
+    }
+    for (; i < i1; ++i) f(i, key_at(i));
+  };
   uint32_t gt = 0, eq = 0;
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint32_t kk = key_at(i);
+  run([&](int64_t, uint32_t kk) {
     gt += kk > kstar;
     eq += kk == kstar;
-  }
+  });
   uint32_t gt_incl = gt, eq_incl = eq, gt_tot = 0, eq_tot = 0;
   block_scan2(gt_incl, eq_incl, gt_tot, eq_tot, sh);
   uint32_t eqc = eq_incl - eq;                   // equal keys before this run
   uint32_t pos = (gt_incl - gt) + min(eqc, need);
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint32_t kk = key_at(i);
+  run([&](int64_t i, uint32_t kk) {
     if (kk > kstar) {
       if (pos < (uint32_t)k) orow[pos] = (int32_t)i;
       ++pos;
@@ -164,7 +208,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       }
       ++eqc;
     }
-  }
+  });
 }
 
 }  // namespace

@@ -400,3 +400,37 @@ def test_topk_crafted_rows():
     rows.append(np.array([np.inf, -np.inf, 1.0, 3.0e38, -3.0e38] * 1000, dtype=np.float32))
     _crafted_topk(rows, 2048)
     _crafted_topk([r[:5000] for r in rows], 7)
+
+
+def test_reference_max_restart_path():
+    """Rows whose logits exceed the first tile's maximum by far more than the softmax headroom
+    force the attention kernel to raise its reference maxima and redo the split; the result must
+    still match the oracle."""
+    case = _small_case("restart", (6000, 9000, 3000), (1, 1, 1), sigma=1.0)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    idx = dsa.topk(scores, batch, case.index_topk)
+    torch.cuda.synchronize()
+    kv = d["kv"][0].clone()
+    rows = DI.query_rows(case)
+    for t, b, p, base in rows:
+        sel = idx[t][idx[t] >= 0].long()
+        late = sel[-3:]                                  # in the last tile of the last split
+        kv[base + late] = (kv[base + late].float() * 40).to(kv.dtype)
+    out, lse = dsa.sparse_mla_fwd(d["q"][0], kv, idx, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for t, b, p, base in rows:
+        sel = idx[t][idx[t] >= 0].cpu().numpy()
+        o, l = O.sparse_attention_row(host64(d["q"][0][t]),
+                                      host64(kv[base + torch.as_tensor(sel, device="cuda")]),
+                                      case.d_v, case.softmax_scale)
+        got.append(out[t].float().cpu().numpy())
+        ref.append(o)
+        assert np.allclose(lse[t].double().cpu().numpy(), l, rtol=1e-4, atol=1e-2)
+    got, ref = np.stack(got), np.stack(ref)
+    # value rows scaled by 40 make outputs ~100x the workload's, so max|d| is taken relative
+    ok, a, rel = attn_close(got, ref, max_abs=2e-2 * np.abs(ref).max())
+    say(f"  restart path: max|d|={a:.3e} (max|ref| {np.abs(ref).max():.1f}) rel={rel:.3e}")
+    assert ok, (a, rel)
