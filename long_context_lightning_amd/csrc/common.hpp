@@ -89,6 +89,39 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// DPP move of v within the wave; lanes without a source, or outside row_mask, read `identity`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes with an associative op and its identity: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then lane 15 of a row is folded into the row above it and lane 31
+// into the upper half.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t identity, Op op) {
+  v = op(v, dpp_u32<0x111>(v, identity));        // row_shr:1
+  v = op(v, dpp_u32<0x112>(v, identity));        // row_shr:2
+  v = op(v, dpp_u32<0x114>(v, identity));        // row_shr:4
+  v = op(v, dpp_u32<0x118>(v, identity));        // row_shr:8
+  v = op(v, dpp_u32<0x142, 0xa>(v, identity));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_u32<0x143, 0xc>(v, identity));   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+struct AddU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct MinU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct MaxU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  return wave_incl_scan(v, 0u, AddU32());
+}
+
+// Value of lane 63 (the wave-wide result of an inclusive scan), as a wave-uniform value.
+__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+
 // Largest b in [0, nseq) with cu[b] <= x (cu ascending, cu[0] <= x).
 template <typename I>
 __device__ __forceinline__ int find_seq(const I* __restrict__ cu, int nseq, int64_t x) {
