@@ -18,8 +18,10 @@
 //   * P*V on 32x32x16 MFMAs: wave w owns heads 32*(w>>1).. and value columns 256*(w&1)..;
 //     P is the A operand, V (row-major in the same LDS tile) is read column-wise with the
 //     gfx950 transposing LDS read. The fp32 output block stays in registers across tiles.
-//   * With several splits per query, each split writes its normalised partial output and
-//     log-sum-exp; a combine kernel merges them with exp(lse_i - lse) weights.
+//   * With several splits per query, each split stores its normalised partial output in bf16,
+//     in the accumulator register layout (32 contiguous bytes per lane and value block), and
+//     its log-sum-exp; a combine kernel merges them with exp(lse_i - lse) weights. With one
+//     split the output block is transposed through LDS and written with 16-byte stores.
 #include <algorithm>
 
 #include "common.hpp"
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
     const int32_t* __restrict__ indices, int k, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int H,
     float scale_log2, int nsplit, int rows_per_split, int tgroups, __bf16* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
@@ -348,27 +350,50 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
   float* fin = (float*)(lds + OFF_R);          // [0,64): l per head, [64,128): max per head
-  __syncthreads();
+  __syncthreads();                             // every wave is done with the stages and P
   if (kh == 0 && half == 0) {
     fin[head_lane] = l_run;
     fin[HG + head_lane] = m_ref;
   }
   __syncthreads();
-  const int head_base = hg * HG + hb * 32;
+  float inv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int hl = hb * 32 + mfma32_row(r, lane);
-    const float l = fin[hl];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t h = head_base + mfma32_row(r, lane);
+    const float l = fin[hb * 32 + mfma32_row(r, lane)];
+    inv[r] = l > 0.f ? 1.f / l : 0.f;
+  }
+  if (nsplit > 1) {
+    // partial output in the accumulator layout: per (wave, value block) each lane stores its
+    // 16 values as 32 contiguous bytes, so a wave writes 2 KB contiguous per block
+    __bf16* po =
+        part_o + ((((int64_t)t * nsplit + split) * (H / HG) + hg) * 4 + wave) * (8 * 1024);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int col = dvh * 256 + db * 32 + c32;
-      const float v = o[db][r] * inv;
-      if (nsplit == 1)
-        out[((int64_t)t * H + h) * DV + col] = (__bf16)v;
-      else
-        part_o[(((int64_t)t * nsplit + split) * H + h) * DV + col] = v;
+      bf16x8 lo8, hi8;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        lo8[r] = (__bf16)(o[db][r] * inv[r]);
+        hi8[r] = (__bf16)(o[db][8 + r] * inv[8 + r]);
+      }
+      *(bf16x8*)(po + (db * 64 + lane) * 16) = lo8;
+      *(bf16x8*)(po + (db * 64 + lane) * 16 + 8) = hi8;
+    }
+  } else {
+    // final output: transpose the [64 heads x 512] block through LDS, then 16-byte stores
+    __bf16* ot = (__bf16*)lds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hl = hb * 32 + mfma32_row(r, lane);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        ot[hl * DV + dvh * 256 + db * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
+    }
+    __syncthreads();
+    __bf16* ob = out + ((int64_t)t * H + hg * HG) * DV;
+#pragma unroll 4
+    for (int i = 0; i < HG * DV / 8 / 256; ++i) {
+      const int piece = i * 256 + tid;
+      *(bf16x8*)(ob + piece * 8) = *(const bf16x8*)(ot + piece * 8);
     }
   }
   if (kh == 0 && dvh == 0 && half == 0) {
@@ -383,36 +408,70 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
   }
 }
 
-// Merge the splits of one (query, head): out = sum_i exp(lse_i - lse) * o_i, lse = logsumexp.
-__global__ __launch_bounds__(128) void mla_combine(const float* __restrict__ part_o,
-                                                   const float* __restrict__ part_lse,
-                                                   int nsplit, int H, __bf16* __restrict__ out,
-                                                   float* __restrict__ lse) {
+// Merges the splits of one (query, head group, wave block, value block): 64 lanes, each with the
+// 16 (head, column) values the sparse kernel's accumulator layout gives it.
+// out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i (natural-log units).
+__global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ part_o,
+                                                  const float* __restrict__ part_lse,
+                                                  int nsplit, int H, __bf16* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  extern __shared__ float wgt[];               // [nsplit][32] merge weights per head
   const int t = blockIdx.x;
-  const int h = blockIdx.y;
-  const float* pl = part_lse + (int64_t)t * nsplit * H + h;
-  float mx = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * H]);
-  float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int i = 0; i < nsplit; ++i) sum += expf(pl[(int64_t)i * H] - mx);
-  const float tot = (mx == -INFINITY) ? -INFINITY : mx + logf(sum);
-  f32x4 acc = {};
-  const int col = threadIdx.x * 4;
-  if (mx != -INFINITY) {
+  const int y = blockIdx.y;
+  const int db = y & 7;
+  const int w = (y >> 3) & 3;
+  const int hg = y >> 5;
+  const int hb = w >> 1, dvh = w & 1;
+  const int lane = threadIdx.x;
+  const int h0 = hg * HG + hb * 32;            // first head of this block
+  // every split's log-sum-exp of the block's 32 heads, one coalesced load per lane and pass
+  for (int j = lane; j < nsplit * 32; j += 64)
+    wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
+  __syncthreads();
+  if (lane < 32) {
+    float mx = -INFINITY;
+    for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, wgt[i * 32 + lane]);
+    float sum = 0.f;
+    if (mx != -INFINITY)
+      for (int i = 0; i < nsplit; ++i) sum += expf(wgt[i * 32 + lane] - mx);
+    const float tot = (mx == -INFINITY) ? -INFINITY : mx + logf(sum);
     for (int i = 0; i < nsplit; ++i) {
-      const float li = pl[(int64_t)i * H];
-      if (li == -INFINITY) continue;
-      const float wgt = expf(li - tot);
-      const f32x4 v = *(const f32x4*)(part_o + (((int64_t)t * nsplit + i) * H + h) * DV + col);
-      acc += wgt * v;
+      const float li = wgt[i * 32 + lane];
+      wgt[i * 32 + lane] = (li == -INFINITY) ? 0.f : expf(li - tot);
     }
+    if (lse && dvh == 0 && db == 0) lse[(int64_t)t * H + h0 + lane] = tot;
   }
-  bf16x4 ob;
+  __syncthreads();
+  float acc[16];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ob[e] = (__bf16)acc[e];
-  *(bf16x4*)(out + ((int64_t)t * H + h) * DV + col) = ob;
-  if (lse && threadIdx.x == 0) lse[(int64_t)t * H + h] = tot;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int64_t stride = (int64_t)(H / HG) * 4 * 8 * 1024;      // elements per (t, split)
+  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((hg * 4 + w) * 8 + db) * 1024 +
+                     lane * 16;
+  auto add = [&](int i, bf16x8 lo8, bf16x8 hi8) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      acc[r] += wgt[i * 32 + mfma32_row(r, lane)] * (float)lo8[r];
+      acc[8 + r] += wgt[i * 32 + mfma32_row(8 + r, lane)] * (float)hi8[r];
+    }
+  };
+  int i = 0;
+  for (; i + 4 <= nsplit; i += 4) {            // four splits' loads in flight at once
+    bf16x8 lo8[4], hi8[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo8[j] = *(const bf16x8*)(po + (i + j) * stride);
+      hi8[j] = *(const bf16x8*)(po + (i + j) * stride + 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add(i + j, lo8[j], hi8[j]);
+  }
+  for (; i < nsplit; ++i)
+    add(i, *(const bf16x8*)(po + i * stride), *(const bf16x8*)(po + i * stride + 8));
+  __bf16* ob =
+      out + ((int64_t)t * H + hg * HG + hb * 32) * DV + dvh * 256 + db * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ob[(int64_t)mfma32_row(r, lane) * DV] = (__bf16)acc[r];
 }
 
 // fp32 path: one workgroup per (query, head); logits of the selected rows live in LDS.
@@ -488,7 +547,8 @@ MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
   const int tiles_per_split = (tiles + nsplit - 1) / nsplit;
   p.rows_per_split = tiles_per_split * TILE;
   p.nsplit = (k + p.rows_per_split - 1) / p.rows_per_split;
-  p.workspace = p.nsplit > 1 ? (size_t)b.total_q * p.nsplit * n_heads * (DV + 1) * sizeof(float)
+  // per split: log-sum-exp (fp32) and the normalised partial output (bf16) of every head
+  p.workspace = p.nsplit > 1 ? (size_t)b.total_q * p.nsplit * n_heads * (sizeof(float) + DV * 2)
                              : 0;
   return p;
 }
@@ -500,11 +560,11 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
   hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bf16,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, MLA_LDS);
   if (e != hipSuccess) return e;
-  float* part_o = nullptr;
   float* part_lse = nullptr;
+  __bf16* part_o = nullptr;
   if (plan.nsplit > 1) {
-    part_o = (float*)workspace;
-    part_lse = part_o + (size_t)b.total_q * plan.nsplit * n_heads * DV;
+    part_lse = (float*)workspace;
+    part_o = (__bf16*)(part_lse + (size_t)b.total_q * plan.nsplit * n_heads);
   }
   const int tgroups = (b.total_q + 7) / 8;
   const int64_t nblocks = (int64_t)8 * tgroups * plan.nsplit * (n_heads / HG);
@@ -514,8 +574,8 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
       (__bf16*)out, lse, part_o, part_lse);
   e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  mla_combine<<<dim3(b.total_q, n_heads), 128, 0, stream>>>(part_o, part_lse, plan.nsplit,
-                                                             n_heads, (__bf16*)out, lse);
+  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 32), 64, plan.nsplit * 32 * sizeof(float),
+                stream>>>(part_o, part_lse, plan.nsplit, n_heads, (__bf16*)out, lse);
   return hipGetLastError();
 }
 
