@@ -71,6 +71,29 @@ def mla_bytes(case):
     return tot
 
 
+def traffic_record(workload, kernel):
+    """HBM bytes per launch of `kernel` measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    from the committed summary profiles/<workload>_hbm_traffic.md; None when the summary is
+    missing or any kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for ln in open(path):
+        if ln.strip().startswith("traffic-record:"):
+            rec = json.loads(ln.strip()[len("traffic-record:"):])
+    if rec is None:
+        return None
+    csrc = os.path.join(ROOT, "long_context_lightning_amd", "csrc")
+    for name, sha in rec["sources_sha256"].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
+    key = "traffic_bytes_per_launch" if kernel == rec["kernel"] else f"{kernel}_traffic_bytes_per_launch"
+    return rec.get(key)
+
+
 def cpu_baseline(case, sets, budget_s):
     """The oracle as it stands, on a bounded sample of decode queries (host copies made before
     each timed query)."""
@@ -194,7 +217,8 @@ def main():
     achieved = dbytes / (dms * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None, "algorithmic_bytes_per_launch": dbytes,
+            "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
+            "algorithmic_bytes_per_launch": dbytes,
             "avg_launch_ms": round(dms, 5)}
     line = {
         "metric": "DSA decode query-tokens/s + achieved HBM GB/s (indexer+top-k+sparse MLA)",
