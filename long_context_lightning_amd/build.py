@@ -37,9 +37,16 @@ COMMON = [
 ]
 
 
+# Per-file additions. The indexer never sees a NaN: compiled without IEEE NaN handling, its
+# ReLU is one v_max_f32 instead of a NaN-quieting v_max plus the maximum.
+EXTRA = {
+    "indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

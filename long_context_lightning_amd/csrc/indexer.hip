@@ -25,6 +25,10 @@ namespace dsa {
 namespace {
 
 constexpr int D = 128;                  // index_head_dim on the bf16 path
+
+// max(x, 0). This file is compiled without IEEE NaN handling (no NaN reaches the indexer), so
+// fmaxf is a single v_max_f32 instead of a NaN-quieting v_max followed by the maximum.
+__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.f); }
 constexpr int DEC_KEYS_PER_WAVE = 256;
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
@@ -71,7 +75,7 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
 #pragma unroll
       for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[hb][st], cur[st], acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], fmaxf(acc[r], 0.f), v);
+      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], relu(acc[r]), v);
     }
     v += __shfl_xor(v, 32, WAVE);
     const int64_t s = s0 + col;
@@ -112,21 +116,32 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   }
 }
 
-constexpr int PF_QW = 4;                // queries per wave
-constexpr int PF_WAVES = 4;
+constexpr int PF_QW = 2;                // queries per wave
+constexpr int PF_WAVES = 8;             // two waves per SIMD: one's MFMAs overlap the other's VALU
+constexpr int PF_THREADS = PF_WAVES * WAVE;
 constexpr int PF_QB = PF_QW * PF_WAVES; // queries per workgroup
 constexpr int PF_KT = 64;               // keys per LDS stage
 constexpr int PF_STAGE = PF_KT * D;     // bf16 elements per stage
+constexpr int PF_NST = 4;               // stages: three tiles load while one computes
+constexpr int PF_LOADS = PF_STAGE * 2 / 16 / PF_THREADS;   // 16-byte loads per thread and tile (2)
+constexpr int PF_STORES = 2 * PF_QW;    // score store instructions per wave and tile (4)
+
+// Scores of lanes that have nothing to store (causally masked keys, keys past the row, queries
+// past the sequence) go here, one slot per (store, lane) in one of 64 copies picked by the
+// workgroup, so that every tile issues the same number of store instructions and the in-order
+// memory counter can be waited on exactly. Never read.
+constexpr int PF_SINKS = 64;
+__device__ float g_score_sink[PF_SINKS * PF_STORES * WAVE];
 
 // grid: x = query blocks of PF_QB over max_seqlen_q, y = sequence, z = key-range splits.
 template <int HB>
-__global__ __launch_bounds__(256, 1) void indexer_prefill_bf16(
+__global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
     const float* __restrict__ w, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
     float* __restrict__ scores, int64_t ld) {
   constexpr int HI = 32 * HB;
-  __shared__ __attribute__((aligned(16))) __bf16 ktile[2][PF_STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 ktile[PF_NST][PF_STAGE];
 
   const int b = blockIdx.y;
   if (b >= nseq) return;
@@ -169,24 +184,47 @@ __global__ __launch_bounds__(256, 1) void indexer_prefill_bf16(
   }
 
   // Stage layout: key row r occupies 16 slots of 16 B; the slot of 16-B chunk c is c ^ (r & 7),
-  // so the 32 rows read by one B-operand load spread over all LDS banks.
-  auto issue = [&](int64_t ti, int stg) {
+  // so the 32 rows read by one B-operand load spread over all LDS banks. Tiles past the range
+  // load key 0 into their (never read) stage so every iteration issues the same loads.
+  auto issue = [&](int64_t ti) {
+    const int stg = (int)(ti % PF_NST);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int slot = c * 256 + tid;
+    for (int c = 0; c < PF_LOADS; ++c) {
+      const int slot = c * PF_THREADS + tid;
       const int row = slot >> 4;
       const int gc = (slot & 15) ^ (row & 7);
-      const int64_t key = min(ti * PF_KT + row, nkeys - 1);
-      global_to_lds16(k_idx + (kb0 + key) * D + gc * 8, &ktile[stg][(c * 256 + wave * 64) * 8]);
+      const int64_t key = ti < tile_end ? min(ti * PF_KT + row, nkeys - 1) : 0;
+      global_to_lds16(k_idx + (kb0 + key) * D + gc * 8,
+                      &ktile[stg][(c * PF_THREADS + wave * 64) * 8]);
     }
   };
+  // one store per (sub, qi) for every lane: both lane halves hold the finished score of key
+  // `col` and write it to the same address; lanes without a score write to the sink
+  float* sink = g_score_sink + (blockIdx.x % PF_SINKS) * (PF_STORES * WAVE) + lane;
+  auto store = [&](int64_t ti, int sub, int qi, float v) {
+    const int64_t s = ti * PF_KT + sub * 32 + col;
+    const int jq = jb + wave * PF_QW + qi;
+    const int64_t p = p_first + wave * PF_QW + qi;
+    const bool own = ti < tile_end && jq < nq && s <= p && s < nkeys;
+    float* dst = own ? scores + (int64_t)(q0 + jq) * ld + s : sink + (sub * PF_QW + qi) * WAVE;
+    __builtin_nontemporal_store(v, dst);
+  };
 
-  issue(tile_beg, 0);
+  // Issue order: the first PF_NST-1 tiles, a full wait, then per iteration [loads of tile
+  // ti+3][PF_STORES stores]. From the fourth iteration on, exactly 2*(PF_LOADS+PF_STORES) +
+  // PF_STORES memory operations follow the loads of the tile being waited for; in the first
+  // three that tile has already landed.
+#pragma unroll
+  for (int j = 0; j < PF_NST - 1; ++j) issue(tile_beg + j);
+  wait_all_memory();
+
   for (int64_t ti = tile_beg; ti < tile_end; ++ti) {
-    const int stg = (int)((ti - tile_beg) & 1);
-    wait_all_memory();
-    __syncthreads();
-    if (ti + 1 < tile_end) issue(ti + 1, stg ^ 1);
+    const int stg = (int)(ti % PF_NST);
+    __builtin_amdgcn_s_waitcnt((((PF_LOADS + PF_STORES) * 2 + PF_STORES) & 15) |
+                               ((((PF_LOADS + PF_STORES) * 2 + PF_STORES) >> 4) << 14) |
+                               (7 << 4) | (0 << 8));   // vmcnt(16), lgkmcnt(0)
+    __syncthreads();                     // tile ti landed for every wave; tile ti-1 consumed
+    issue(ti + PF_NST - 1);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int row = sub * 32 + col;
@@ -196,7 +234,6 @@ __global__ __launch_bounds__(256, 1) void indexer_prefill_bf16(
         const int chunk = st * 2 + half;
         bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
       }
-      const int64_t s = ti * PF_KT + row;
 #pragma unroll
       for (int qi = 0; qi < PF_QW; ++qi) {
         float v = 0.f;
@@ -206,13 +243,10 @@ __global__ __launch_bounds__(256, 1) void indexer_prefill_bf16(
 #pragma unroll
           for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[qi][hb][st], bop[st], acc);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], fmaxf(acc[r], 0.f), v);
+          for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], relu(acc[r]), v);
         }
         v += __shfl_xor(v, 32, WAVE);
-        const int jq = jb + wave * PF_QW + qi;
-        const int64_t p = p_first + wave * PF_QW + qi;
-        if (half == 0 && jq < nq && s <= p && s < nkeys)
-          scores[(int64_t)(q0 + jq) * ld + s] = v;
+        store(ti, sub, qi, v);
       }
     }
   }
@@ -255,11 +289,11 @@ hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_
     splits = std::max(1, std::min(splits, 8));
     dim3 grid(qblocks, b.nseq, splits);
     if (index_n_heads == 32)
-      indexer_prefill_bf16<1><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
-                                                        b.total_q, b.total_k, scores, ld);
+      indexer_prefill_bf16<1><<<grid, PF_THREADS, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                               b.total_q, b.total_k, scores, ld);
     else
-      indexer_prefill_bf16<2><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
-                                                        b.total_q, b.total_k, scores, ld);
+      indexer_prefill_bf16<2><<<grid, PF_THREADS, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
+                                                               b.total_q, b.total_k, scores, ld);
   } else {
     dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK), b.max_q);
     if (index_n_heads == 32)
