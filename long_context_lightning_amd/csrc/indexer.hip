@@ -8,10 +8,11 @@
 // heads inside each lane (16 head rows per lane) plus one cross-lane exchange between the two
 // lane halves; lanes 0..31 then hold the 32 finished scores of the tile.
 //
-//  * decode kernel: few queries per sequence. Each wave streams 256 consecutive key rows of the
-//    flattened key cache straight from HBM into registers (B operand), double-buffered, with the
-//    query's heads resident in registers (A operand). Work is laid over the flattened key rows,
-//    so ragged batches with very different lengths need no padding.
+//  * decode kernel: few queries per sequence. A workgroup owns 1024 consecutive rows of the
+//    flattened key cache; its 4 waves take every fourth 32-key step of each sequence segment in
+//    it, so the workgroup reads one contiguous stream. Key rows go straight from HBM into
+//    registers (B operand), two steps ahead, with the query's heads resident (A operand). Work is
+//    laid over the flattened key rows, so ragged batches need no padding.
 //  * prefill kernel: many queries per sequence (chunked prefill). A workgroup owns 16 queries
 //    (4 per wave, A operands in registers) and walks the causal key range in 64-key tiles staged
 //    in LDS with direct global->LDS loads, double-buffered; each B fragment read from LDS feeds 4
@@ -33,12 +34,17 @@ constexpr int DEC_KEYS_PER_WAVE = 256;
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
 
+constexpr int DEC_STEP = 32;            // keys per MFMA step
+
+// Streams key rows s_beg, s_beg + stride, .. (32-key steps) of one sequence for query t, below
+// s_end. Each lane loads the 256-byte row of its key column straight into registers (the B
+// operand), two steps ahead of the MFMAs, so about 16 KB per wave are in flight.
 template <int HB>
 __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
                                                const __bf16* __restrict__ k_idx,
                                                const float* __restrict__ w, int t, int64_t kb0,
                                                int64_t s_beg, int64_t s_end,
-                                               float* __restrict__ srow) {
+                                               float* __restrict__ srow, int stride) {
   constexpr int HI = 32 * HB;
   const int lane = lane_id();
   const int half = lane >> 5;
@@ -56,32 +62,41 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
   }
 
   const __bf16* kb = k_idx + kb0 * D + half * 8;
-  bf16x8 cur[8], nxt[8];
-  {
-    const int64_t s = min(s_beg + col, s_end - 1);
+  auto load = [&](int64_t s0, bf16x8* dst) {
+    const int64_t s = min(s0 + col, s_end - 1);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) cur[st] = *(const bf16x8*)(kb + s * D + st * 16);
-  }
-  for (int64_t s0 = s_beg; s0 < s_end; s0 += 32) {
-    if (s0 + 32 < s_end) {
-      const int64_t s = min(s0 + 32 + col, s_end - 1);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) nxt[st] = *(const bf16x8*)(kb + s * D + st * 16);
-    }
+    for (int st = 0; st < 8; ++st) dst[st] = *(const bf16x8*)(kb + s * D + st * 16);
+  };
+  auto step = [&](int64_t s0, const bf16x8* bop) {
     float v = 0.f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       f32x16 acc = {};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[hb][st], cur[st], acc);
+      for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[hb][st], bop[st], acc);
 #pragma unroll
       for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], relu(acc[r]), v);
     }
     v += __shfl_xor(v, 32, WAVE);
     const int64_t s = s0 + col;
     if (half == 0 && s < s_end) srow[s] = v;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) cur[st] = nxt[st];
+  };
+  // three buffers with fixed register names (a rotating copy would wait for the loads), so
+  // two steps of key rows stay in flight while one is multiplied
+  bf16x8 b0[8], b1[8], b2[8];
+  if (s_beg >= s_end) return;
+  load(s_beg, b0);
+  load(min(s_beg + stride, s_end - 1), b1);
+  load(min(s_beg + 2 * stride, s_end - 1), b2);
+  for (int64_t s0 = s_beg; s0 < s_end; s0 += 3 * stride) {
+    step(s0, b0);
+    if (s0 + stride >= s_end) break;
+    load(min(s0 + 3 * stride, s_end - 1), b0);
+    step(s0 + stride, b1);
+    if (s0 + 2 * stride >= s_end) break;
+    load(min(s0 + 4 * stride, s_end - 1), b1);
+    step(s0 + 2 * stride, b2);
+    load(min(s0 + 5 * stride, s_end - 1), b2);
   }
 }
 
@@ -94,8 +109,8 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     float* __restrict__ scores, int64_t ld) {
   const int wave = threadIdx.x >> 6;
   const int j = blockIdx.y;
-  int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK + (int64_t)wave * DEC_KEYS_PER_WAVE;
-  const int64_t f_end = min(f + DEC_KEYS_PER_WAVE, total_k);
+  int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
+  const int64_t f_end = min(f + DEC_KEYS_PER_BLOCK, total_k);
   while (f < f_end) {
     const int b = find_seq_wave(cu_k, nseq, f);
     const int64_t kb0 = cu_k[b];
@@ -109,8 +124,8 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
       const int64_t p = (kb1 - kb0) - nq + j;
       const int64_t s_beg = f - kb0;
       const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
-      if (s_beg < s_end)
-        decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg, s_end, scores + (int64_t)t * ld);
+      decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg + DEC_STEP * wave, s_end,
+                         scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES);
     }
     f = seg_end;
   }
