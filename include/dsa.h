@@ -32,7 +32,7 @@
  *   - A failed kernel launch returns DSA_ERR_HIP; the HIP error stays readable through
  *     hipGetLastError().
  *   - Supported shapes: bf16 with (d_qk, d_v, index_head_dim) = (576, 512, 128),
- *     n_heads a multiple of 64, index_n_heads 32 or 64; fp32 with d_qk <= 1024, d_v <= d_qk,
+ *     n_heads a multiple of 32, index_n_heads 32 or 64; fp32 with d_qk <= 1024, d_v <= d_qk,
  *     index_head_dim <= 256, n_heads <= 1024, index_n_heads <= 128. Other combinations return
  *     DSA_ERR_UNSUPPORTED.
  */

@@ -58,7 +58,7 @@ dsa_status check_mla(const dsa_batch* b, const void* q, const void* kv, const in
       dv <= 0 || dv > dqk || !(scale == scale))
     return DSA_ERR_INVALID_ARG;
   if (dt == DSA_BF16) {
-    if (dqk != 576 || dv != 512 || h % 64 != 0) return DSA_ERR_UNSUPPORTED;
+    if (dqk != 576 || dv != 512 || h % 32 != 0) return DSA_ERR_UNSUPPORTED;
   } else if (dt == DSA_F32) {
     if (dqk > 1024 || h > 1024 || k > dsa::kMaxF32TopK) return DSA_ERR_UNSUPPORTED;
   } else {
@@ -139,7 +139,7 @@ size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,
   if (!batch_ok(batch) || index_topk <= 0) return 0;
   const Batch b = to_batch(batch);
   // only the bf16 (d_v = 512) sparse-MLA kernel splits the selected rows and needs scratch
-  const bool split_kv = n_heads > 0 && n_heads % 64 == 0 && d_v == 512;
+  const bool split_kv = n_heads > 0 && n_heads % 32 == 0 && d_v == 512;
   const size_t mla = split_kv ? mla_ws(batch, index_topk, n_heads, DSA_BF16) : 0;
   switch (op) {
     case DSA_OP_INDEXER:

@@ -1,23 +1,24 @@
 // Sparse MLA forward in MQA mode ("How GLM5.3 Sparse Attention Affects HBM Memory Usage",
 // How it works / Model): every query head attends, with softmax, over only the top-k selected
 // latent rows; the key is the full 576-wide latent+rope row and the value its leading 512
-// columns (weight absorption), so one gathered 1152-byte row serves all 64 heads for both
-// products.
+// columns (weight absorption), so one gathered 1152-byte row serves all heads for both products.
 //
-// bf16 kernel: one workgroup = (query, KV split, group of 64 heads), 4 waves.
-//   * Tiles of 64 selected rows are gathered straight from HBM into LDS with direct
-//     global->LDS 16-byte loads (double-buffered: tile i+1 streams in while tile i computes).
-//     Each row's 72 chunks of 16 B are stored with the chunk slot XOR-ed by a 3-bit function
-//     of the row (swz) that keeps every MFMA operand read free of LDS bank conflicts.
+// bf16 kernel: one workgroup = (query, KV split, group of 32 heads), 4 waves, 80 KB of LDS, so
+// two workgroups share a CU. The two head groups of one (query, split) sit next to each other
+// on one XCD and gather the same rows at about the same time: the second read comes from L2.
+//   * Tiles of 64 selected rows are gathered straight from HBM into one LDS stage with direct
+//     global->LDS 16-byte loads; the other workgroup on the CU computes while one waits. Each
+//     row's 72 chunks of 16 B are stored with the chunk slot XOR-ed by a 3-bit function of the
+//     row (swz) that keeps every MFMA operand read free of LDS bank conflicts.
 //   * QK^T is computed transposed, S^T[rows x heads] = KV[rows x 576] * Q^T, on 32x32x16 MFMAs:
-//     wave w owns rows 32*(w&1).. and heads 32*(w>>1)..; the query block is resident in
-//     registers (B operand) and KV rows are the A operand read from LDS. In this layout each
-//     lane holds one head and 16 rows, so the softmax max / sum are in-lane plus one exchange.
-//   * Online softmax in fp32 (base-2 exponent, scale*log2(e) folded into the logits); P is
-//     rounded to bf16 into LDS.
-//   * P*V on 32x32x16 MFMAs: wave w owns heads 32*(w>>1).. and value columns 256*(w&1)..;
-//     P is the A operand, V (row-major in the same LDS tile) is read column-wise with the
-//     gfx950 transposing LDS read. The fp32 output block stays in registers across tiles.
+//     wave (rb, kh) owns rows 32*rb.. and K half kh for all 32 heads; the query half is resident
+//     in registers (B operand). The two K-half partial sums of a row block are exchanged through
+//     LDS, each wave keeping half of the block's elements, so every lane holds one head.
+//   * Softmax in fp32 (base-2 exponent, scale*log2(e) folded into the logits) against a fixed
+//     reference maximum per head; P is rounded to bf16 into LDS.
+//   * P*V on 32x32x16 MFMAs: wave w owns value columns 128*w.. of all 32 heads; P is the A
+//     operand, V (row-major in the same LDS tile) is read column-wise with the gfx950
+//     transposing LDS read. The fp32 output block stays in registers across tiles.
 //   * With several splits per query, each split stores its normalised partial output in bf16,
 //     in the accumulator register layout (32 contiguous bytes per lane and value block), and
 //     its log-sum-exp; a combine kernel merges them with exp(lse_i - lse) weights. With one
@@ -32,21 +33,22 @@ namespace {
 
 constexpr int DQK = 576;
 constexpr int DV = 512;
-constexpr int HG = 64;                       // heads per workgroup
+constexpr int HG = 32;                       // heads per workgroup
 constexpr int TILE = 64;                     // selected rows per LDS stage
 constexpr int ROWB = DQK * 2;                // 1152 bytes per latent row
 constexpr int CHUNKS = ROWB / 16;            // 72 chunks of 16 B
 constexpr int STAGE_BYTES = TILE * ROWB;     // 73728
 constexpr int ROPE_OFF = DV * 2;             // byte offset of the RoPE columns in a row
 constexpr int P_STRIDE = TILE + 8;           // bf16 elements per head row of P (padded)
-constexpr int OFF_R = 2 * STAGE_BYTES;       // 16 KB: QK half-sum exchange, then P
-constexpr int R_BYTES = 16384;
-constexpr int MLA_LDS = OFF_R + R_BYTES;     // 160 KB
+constexpr int OFF_R = STAGE_BYTES;           // 8 KB: QK half-sum exchange, then P
+constexpr int R_BYTES = 4 * 8 * 64 * 4;      // 8 floats per lane per wave
+constexpr int MLA_LDS = OFF_R + R_BYTES;     // 80 KB: two workgroups per CU
 constexpr int LOADS_PER_THREAD = STAGE_BYTES / 16 / 256;   // 18
 constexpr int QK_STEPS = DQK / 16 / 2;       // 18 MFMA k-steps per K half
+constexpr int VB_WAVE = DV / 32 / 4;         // 4 value blocks of 32 columns per wave
 static_assert(LOADS_PER_THREAD * 256 * 16 == STAGE_BYTES, "stage must split evenly");
-static_assert(HG * P_STRIDE * 2 <= R_BYTES && 4 * 16 * 64 * 4 == R_BYTES, "R region");
-static_assert(MLA_LDS <= 160 * 1024, "LDS budget");
+static_assert(HG * P_STRIDE * 2 <= R_BYTES, "P fits the exchange region");
+static_assert(2 * MLA_LDS <= 160 * 1024, "two workgroups per CU");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -66,39 +68,37 @@ __device__ __forceinline__ int swz(int r) {
 // instead of occupying registers across the tile loop.
 __device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
 
-// s_waitcnt vmcnt(N) with the other counters left alone (GFX9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Softmax statistics live in the RoPE columns of the tile being processed: those columns are
 // only read by QK^T, which every wave has finished before the first statistic is written.
 // Float i sits in row i/32 at RoPE byte 4*(i%32).
 __device__ __forceinline__ float* stat(char* stage, int i) {
   return (float*)(stage + (i >> 5) * ROWB + ROPE_OFF + (i & 31) * 4);
 }
-constexpr int ST_MAX = 0;       // [2][HG] per row-block tile maximum
-constexpr int ST_SUM = 128;     // [2][HG] per row-block tile sum
-constexpr int ST_FLAG = 256;    // [4]     wave saw a tile beyond its reference headroom
+constexpr int ST_MAX = 0;       // [4 waves][HG] maximum over each wave's 16 rows
+constexpr int ST_SUM = 128;     // [4 waves][HG] sums over the same rows
+constexpr int ST_FLAG = 256;    // [4]           wave saw a logit beyond its reference headroom
 
-// grid: 1-D, 8 * ceil(T/8) * nsplit * (H/64) workgroups. Consecutive workgroups are dispatched
-// round-robin to the 8 XCDs; the mapping below gives all splits of one query the same XCD so
-// its query block is fetched into that XCD's L2 once.
-__global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
+// Element r of the QK accumulator kept by K-half wave kh after the exchange: value q (0..7) of
+// the wave is element 8*(q/4) + 4*kh + q%4; the other eight go to the partner wave.
+__device__ __forceinline__ int kept_elem(int q, int kh) { return 8 * (q >> 2) + 4 * kh + (q & 3); }
+
+// grid: 1-D, 8 * ceil(T/8) * nsplit * (H/32) workgroups. Consecutive workgroups are dispatched
+// round-robin to the 8 XCDs; the mapping gives every workgroup of one query the same XCD, and
+// puts the two head halves of one (query, split) next to each other there, so the second read
+// of each gathered row is served by that XCD's L2.
+__global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ indices, int k, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int H,
     float scale_log2, int nsplit, int rows_per_split, int tgroups, __bf16* __restrict__ out,
     float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nhg = H / HG;
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
-  const int split = kk % nsplit;
-  const int rest = kk / nsplit;
-  const int t = (rest % tgroups) * 8 + xcd;
-  const int hg = rest / tgroups;
+  const int hg = kk % nhg;
+  const int split = (kk / nhg) % nsplit;
+  const int t = (kk / nhg / nsplit) * 8 + xcd;
   if (t >= total_q) return;
 
   const int tid = threadIdx.x;
@@ -106,11 +106,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c32 = lane & 31;
-  const int kh = wave & 1;        // QK: K half (columns 288*kh ..)
-  const int hb = wave >> 1;       // QK and PV: head block within the group
-  const int rb = kh;              // after the half-sum exchange: row block owned
-  const int dvh = wave & 1;       // PV: value-column half
-  const int head_lane = hb * 32 + c32;   // head (within the group) of this lane's softmax stats
+  const int kh = wave & 1;        // QK: K half (columns 288*kh ..); softmax: kept element set
+  const int rb = wave >> 1;       // QK: row block (rows 32*rb ..)
+  const int cq = wave;            // PV: value columns 128*cq ..
 
   const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, t);
   const int64_t L = qp.len;
@@ -120,30 +118,36 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
   const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const int32_t* irow = indices + (int64_t)t * k;
   const __bf16* kvb = kv + qp.key_base * DQK;
-  __bf16* pl = (__bf16*)(lds + OFF_R);        // [HG][P_STRIDE]
-  float* xch = (float*)(lds + OFF_R);         // [4 waves][16][64]
+  char* stage = lds;
+  float* xch = (float*)(lds + OFF_R);         // [4 waves][8][64]
+  __bf16* pl = (__bf16*)(lds + OFF_R);        // [HG][P_STRIDE], after the exchange is read
 
   // Softmax with a fixed reference maximum per head: the first tile in which a head has a finite
   // logit sets its reference m_ref, and probabilities are exp2(s - m_ref) without rescaling the
   // output block. If a later tile exceeds a reference by more than 2^kHeadroom, the workgroup
   // raises the references and restarts its split (softmax is shift-invariant, so the result is
-  // the same). This keeps every update of the output accumulators inside the MFMA pipe.
-  f32x16 o[8];
+  // the same). Every update of the output accumulators stays in the MFMA pipe.
+  f32x16 o[VB_WAVE];
   float m_ref = -INFINITY, l_run = 0.f;
+  auto zero_o = [&]() {                       // 0 x 0 + 0 on the matrix core keeps o in AGPRs
+    const bf16x8 z = {};
+#pragma unroll
+    for (int db = 0; db < VB_WAVE; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
+  };
+  zero_o();
 
   if (ntiles > 0) {
-    // index of tile row `lane`; always issues one load so the vmcnt bookkeeping is uniform
+    // index of tile row `lane`, -1 past the split
     auto load_idx = [&](int tile) -> int {
       const int r = r_beg + tile * TILE + lane;
       const int v = irow[min(r, k - 1)];
       return (tile < ntiles && r < r_end) ? v : -1;
     };
     // gathers one tile: slot c*256+tid of the stage holds chunk (slot%72)^swz(row) of row
-    // slot/72; always issues LOADS_PER_THREAD loads (invalid rows read row 0, masked later)
-    auto issue = [&](int idxv, int stg) {
-      char* base = lds + stg * STAGE_BYTES;
+    // slot/72 (invalid rows read row 0 and are masked later)
+    auto issue = [&](int idxv) {
       int tt = tid;
-      opaque(tt);                            // recomputed per tile instead of held in registers
+      opaque(tt);
 #pragma unroll
       for (int g = 0; g < LOADS_PER_THREAD / 6; ++g) {
         int vs[6], gcs[6];
@@ -158,125 +162,78 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
         for (int j = 0; j < 6; ++j) {
           const uint32_t v = (uint32_t)vs[j] < Lu ? (uint32_t)vs[j] : 0u;
           global_to_lds16(kvb + (size_t)v * DQK + gcs[j] * 8,
-                          base + ((g * 6 + j) * 256 + wave * 64) * 16);
+                          stage + ((g * 6 + j) * 256 + wave * 64) * 16);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the groups apart: bounded live registers
       }
     };
 
-    const int idx0 = load_idx(0);
-    const int idx1 = load_idx(1);
-    issue(idx0, 0);                          // tile 0 in flight before the query block loads
     bf16x8 qreg[QK_STEPS];
     {
-      const __bf16* qr = q + ((int64_t)t * H + hg * HG + head_lane) * DQK +
-                         kh * (QK_STEPS * 16) + half * 8;
+      const __bf16* qr = q + ((int64_t)t * H + hg * HG + c32) * DQK + kh * (QK_STEPS * 16) +
+                         half * 8;
 #pragma unroll
       for (int i = 0; i < QK_STEPS; ++i) qreg[i] = *(const bf16x8*)(qr + i * 16);
     }
-    // A-operand lane bases: step i of this wave reads chunk 36*kh + 2*i + half of rows c32 and
-    // 32 + c32 (same swizzle); with u = 2*kh + i the slot is
-    // 8*(4*kh + u/4) + ((2*(u%4) + half) ^ swz): four lane bases plus 128*(i/4) immediates.
+    int idx_cur = load_idx(0);
+    wait_all_memory();
+    issue(idx_cur);
+    // A-operand lane bases: step i reads chunk 36*kh + 2*i + half of row 32*rb + c32; with
+    // u = 2*kh + i the slot is 8*(4*kh + u/4) + ((2*(u%4) + half) ^ swz): four lane bases plus
+    // 128*(i/4) immediates.
     const int sw = swz(c32);
     int abase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int u = 2 * kh + j;
-      abase[j] = c32 * ROWB + 128 * (4 * kh + (u >> 2)) + (((2 * (u & 3) + half) ^ sw) << 4);
+      abase[j] = (32 * rb + c32) * ROWB + 128 * (4 * kh + (u >> 2)) +
+                 (((2 * (u & 3) + half) ^ sw) << 4);
     }
 
-    // zeroes the output block with MFMAs (0 x 0 + 0) so every definition of o stays in the
-    // matrix-core register class
-    auto zero_o = [&]() {
-      const bf16x8 z = {};
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
-    };
-    zero_o();
-    issue(idx1, 1);                          // tiles 0 and 1 in flight before the loop
-    int idx_cur = idx1;                      // indices of the newest issued tile
-    int idx_next = load_idx(2);
-
     for (int tile = 0; tile < ntiles; ++tile) {
-      const int stg = tile & 1;
-      if (tile == 0) wait_vmcnt<LOADS_PER_THREAD + 1>();   // tile 1 and idx 2 may be in flight
-      else wait_vmcnt<1>();                                // the next index load may be in flight
-      __syncthreads();                       // tile rows landed; previous tile fully consumed
-      const int idx_tile = tile == 0 ? idx0 : (tile == 1 ? idx1 : idx_cur);
-      // The next tile's gathers go out one per QK step (below) so the wave never stalls on a
-      // burst of 18 loads; their row indices are fetched from the index register first.
-      const bool do_issue = tile >= 1 && tile + 1 < ntiles;
-      int tt = tid;
-      opaque(tt);
-      int nv[LOADS_PER_THREAD];
-      if (do_issue) {
-#pragma unroll
-        for (int c = 0; c < LOADS_PER_THREAD; ++c)
-          nv[c] = __shfl(idx_next, (c * 256 + tt) / CHUNKS, WAVE);
-      }
-      char* nbase = lds + (stg ^ 1) * STAGE_BYTES;
-      auto issue_one = [&](int c) {
-        const int slot = c * 256 + tt;
-        const int row = slot / CHUNKS;
-        const int gc = (slot - row * CHUNKS) ^ swz(row);
-        const uint32_t v = (uint32_t)nv[c] < Lu ? (uint32_t)nv[c] : 0u;
-        global_to_lds16(kvb + (size_t)v * DQK + gc * 8, nbase + (c * 256 + wave * 64) * 16);
-      };
-      char* sbase = lds + stg * STAGE_BYTES;
-      const uint64_t vmask =
-          __ballot(r_beg + tile * TILE + lane < r_end && (uint32_t)idx_tile < Lu);
+      const int idx_nxt = load_idx(tile + 1);
+      wait_all_memory();                       // this tile's gathers (and the index load)
+      __syncthreads();
+      const uint64_t vmask = __ballot((uint32_t)idx_cur < Lu);
 
-      // ---- QK^T half sums: S^T[64 rows x 32 heads] over this wave's 288 columns
-      f32x16 s0 = {}, s1 = {};
+      // ---- QK^T half sums: S^T[32 rows x 32 heads] over this wave's 288 columns
+      f32x16 s = {};
       {
-        bf16x8 a0[2], a1[2];
-        auto rd = [&](int i, int b) {
-          const char* pa = sbase + abase[i & 3] + (i >> 2) * 128;
-          a0[b] = *(const bf16x8*)pa;
-          a1[b] = *(const bf16x8*)(pa + 32 * ROWB);
-        };
-        static_assert(QK_STEPS == LOADS_PER_THREAD, "one gather per QK step");
+        bf16x8 a[2];
+        auto rd = [&](int i, int b) { a[b] = *(const bf16x8*)(stage + abase[i & 3] + (i >> 2) * 128); };
         rd(0, 0);
 #pragma unroll
         for (int i = 0; i < QK_STEPS; ++i) {
           if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
-          if (do_issue) issue_one(i);
-          s0 = mfma32x32x16(a0[i & 1], qreg[i], s0);
-          s1 = mfma32x32x16(a1[i & 1], qreg[i], s1);
+          s = mfma32x32x16(a[i & 1], qreg[i], s);
         }
       }
-      if (tile >= 1) {
-        if (do_issue) idx_cur = idx_next;
-        idx_next = load_idx(tile + 2);
-      }
-      // ---- exchange half sums: keep row block kh, hand the other to the partner wave
-      const f32x16 give = kh ? s0 : s1;
-      f32x16 s = kh ? s1 : s0;
+      // ---- exchange half sums: keep element set kh, hand the other to the partner wave
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = give[r];
+      for (int qi = 0; qi < 8; ++qi) xch[(wave * 8 + qi) * 64 + lane] = s[kept_elem(qi, kh ^ 1)];
       __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
-
-      float sv[16];
+      float sv[8];
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb * 32 + mfma32_row(r, lane);
-        sv[r] = ((vmask >> row) & 1) ? s[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
+      for (int qi = 0; qi < 8; ++qi) {
+        const int e = kept_elem(qi, kh);
+        const float v = s[e] + xch[((wave ^ 1) * 8 + qi) * 64 + lane];
+        const int row = 32 * rb + mfma32_row(e, lane);
+        sv[qi] = ((vmask >> row) & 1) ? v * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[qi]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      if (half == 0) *stat(sbase, ST_MAX + rb * HG + head_lane) = mx;
-      __syncthreads();
+      if (half == 0) *stat(stage, ST_MAX + wave * HG + c32) = mx;
+      __syncthreads();                         // the exchange region is free for P from here
       const float m_tile =
-          fmaxf(*stat(sbase, ST_MAX + head_lane), *stat(sbase, ST_MAX + HG + head_lane));
+          fmaxf(fmaxf(*stat(stage, ST_MAX + 0 * HG + c32), *stat(stage, ST_MAX + 1 * HG + c32)),
+                fmaxf(*stat(stage, ST_MAX + 2 * HG + c32), *stat(stage, ST_MAX + 3 * HG + c32)));
       const bool exceed = m_ref != -INFINITY && m_tile > m_ref + kHeadroom;
       if (m_ref == -INFINITY || exceed) m_ref = m_tile;
       const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       float ls = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 2; ++g) {
         bf16x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -285,90 +242,92 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
           ls += p;
           pk[e] = (__bf16)p;
         }
-        const int row0 = rb * 32 + 8 * g + 4 * half;
-        *(bf16x4*)(pl + head_lane * P_STRIDE + row0) = pk;
+        const int row0 = 32 * rb + 16 * g + 8 * kh + 4 * half;
+        *(bf16x4*)(pl + c32 * P_STRIDE + row0) = pk;
       }
       ls += __shfl_xor(ls, 32, WAVE);
-      if (half == 0) *stat(sbase, ST_SUM + rb * HG + head_lane) = ls;
+      if (half == 0) *stat(stage, ST_SUM + wave * HG + c32) = ls;
       const bool wave_exceeds = __ballot(exceed) != 0;   // ballot with every lane active
-      if (lane == 0) *stat(sbase, ST_FLAG + wave) = wave_exceeds ? 1.f : 0.f;
+      if (lane == 0) *stat(stage, ST_FLAG + wave) = wave_exceeds ? 1.f : 0.f;
       __syncthreads();
-      const bool restart = (*stat(sbase, ST_FLAG + 0) + *stat(sbase, ST_FLAG + 1) +
-                            *stat(sbase, ST_FLAG + 2) + *stat(sbase, ST_FLAG + 3)) != 0.f;
-      if (restart) {                       // uniform across the workgroup: redo the split
-        wait_all_memory();                 // drain this pass's gathers before reusing stages
+      const bool restart = (*stat(stage, ST_FLAG + 0) + *stat(stage, ST_FLAG + 1) +
+                            *stat(stage, ST_FLAG + 2) + *stat(stage, ST_FLAG + 3)) != 0.f;
+      if (restart) {                           // uniform across the workgroup: redo the split
+        wait_all_memory();
         __syncthreads();
         zero_o();
         l_run = 0.f;
-        issue(idx0, 0);
-        issue(idx1, 1);
-        idx_cur = idx1;
-        idx_next = load_idx(2);
+        idx_cur = load_idx(0);
+        wait_all_memory();
+        issue(idx_cur);
         tile = -1;
         continue;
       }
-      l_run += *stat(sbase, ST_SUM + head_lane) + *stat(sbase, ST_SUM + HG + head_lane);
+      l_run += (*stat(stage, ST_SUM + 0 * HG + c32) + *stat(stage, ST_SUM + 1 * HG + c32)) +
+               (*stat(stage, ST_SUM + 2 * HG + c32) + *stat(stage, ST_SUM + 3 * HG + c32));
 
-      // ---- O[32 heads x 256 cols] += P[32 heads x 64 rows] * V[64 rows x 256 cols]
-      // V[krow][col] for the B operand of value block db (32 columns), rows 4*rr.. of the
+      // ---- O[32 heads x 128 cols] += P[32 heads x 64 rows] * V[64 rows x 128 cols]
+      // V[krow][col] for the B operand of value block blk (32 columns), rows 4*rr.. of the
       // lane's k-group: krow = 16*ks + rw0 + 4*rr with rw0 = 8*(g16/2) + j16/4, and chunk(col)
-      // = 4*blk + c2 with blk = 8*dvh + db. swz(rw0 + 4) = swz(rw0) ^ 1 and both share bit 2
-      // (b2), so slot = 4*(blk ^ b2) + (c2 ^ (swz & 3)): per (rr, parity of blk) one lane
-      // base, the rest immediate offsets.
-      const int g16 = lane >> 4;
-      const int j16 = lane & 15;
-      const int c2 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-      const int rw0 = 8 * (g16 >> 1) + (j16 >> 2);
-      const int sw0 = swz(rw0);
-      const int b2 = sw0 >> 2;
-      const char* vb[2][2];
+      // = 4*blk + c2 with blk = 4*cq + db. swz(rw0 + 4) = swz(rw0) ^ 1 and both share bit 2
+      // (b2), so slot = 4*(blk ^ b2) + (c2 ^ (swz & 3)): per (rr, parity of blk) one lane base,
+      // the rest immediate offsets.
+      {
+        const int g16 = lane >> 4;
+        const int j16 = lane & 15;
+        const int c2 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+        const int rw0 = 8 * (g16 >> 1) + (j16 >> 2);
+        const int sw0 = swz(rw0);
+        const int b2 = sw0 >> 2;
+        const char* vb[2][2];
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const char* p = sbase + (rw0 + 4 * rr) * ROWB + ((c2 ^ ((sw0 ^ rr) & 3)) << 4) +
-                        (j16 & 1) * 8;
-        vb[rr][0] = p + 64 * b2;     // even blk: blk ^ b2 = blk + b2
-        vb[rr][1] = p - 64 * b2;     // odd blk:  blk ^ b2 = blk - b2
-      }
-      const __bf16* pbase = pl + head_lane * P_STRIDE + half * 8;
+        for (int rr = 0; rr < 2; ++rr) {
+          const char* pp = stage + (rw0 + 4 * rr) * ROWB + ((c2 ^ ((sw0 ^ rr) & 3)) << 4) +
+                           (j16 & 1) * 8;
+          vb[rr][0] = pp + 64 * b2;    // even blk: blk ^ b2 = blk + b2
+          vb[rr][1] = pp - 64 * b2;    // odd blk:  blk ^ b2 = blk - b2
+        }
+        const __bf16* pbase = pl + c32 * P_STRIDE + half * 8;
 #pragma unroll
-      for (int ks = 0; ks < TILE / 16; ++ks) {
-        const bf16x8 pa = *(const bf16x8*)(pbase + ks * 16);
+        for (int ks = 0; ks < TILE / 16; ++ks) {
+          const bf16x8 pa = *(const bf16x8*)(pbase + ks * 16);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const int blk = 8 * dvh + db;
-          const i16x4 v0 = lds_read_tr16(vb[0][db & 1] + ks * 16 * ROWB + (blk << 6));
-          const i16x4 v1 = lds_read_tr16(vb[1][db & 1] + ks * 16 * ROWB + (blk << 6));
-          o[db] = mfma32x32x16(pa, concat_bf16(v0, v1), o[db]);
+          for (int db = 0; db < VB_WAVE; ++db) {
+            const int blk = VB_WAVE * cq + db;
+            const i16x4 v0 = lds_read_tr16(vb[0][db & 1] + ks * 16 * ROWB + (blk << 6));
+            const i16x4 v1 = lds_read_tr16(vb[1][db & 1] + ks * 16 * ROWB + (blk << 6));
+            o[db] = mfma32x32x16(pa, concat_bf16(v0, v1), o[db]);
+          }
         }
       }
+      // the stage and P are free once every wave is past this point: next tile's gathers
+      __syncthreads();
+      if (tile + 1 < ntiles) issue(idx_nxt);
+      idx_cur = idx_nxt;
     }
-  } else {
-    const bf16x8 z = {};
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
   }
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
-  float* fin = (float*)(lds + OFF_R);          // [0,64): l per head, [64,128): max per head
-  __syncthreads();                             // every wave is done with the stages and P
-  if (kh == 0 && half == 0) {
-    fin[head_lane] = l_run;
-    fin[HG + head_lane] = m_ref;
+  float* fin = (float*)(lds + OFF_R);          // [0,32): l per head, [32,64): max per head
+  __syncthreads();
+  if (wave == 0 && half == 0) {
+    fin[c32] = l_run;
+    fin[HG + c32] = m_ref;
   }
   __syncthreads();
   float inv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float l = fin[hb * 32 + mfma32_row(r, lane)];
+    const float l = fin[mfma32_row(r, lane)];
     inv[r] = l > 0.f ? 1.f / l : 0.f;
   }
   if (nsplit > 1) {
     // partial output in the accumulator layout: per (wave, value block) each lane stores its
     // 16 values as 32 contiguous bytes, so a wave writes 2 KB contiguous per block
-    __bf16* po =
-        part_o + ((((int64_t)t * nsplit + split) * (H / HG) + hg) * 4 + wave) * (8 * 1024);
+    __bf16* po = part_o + ((((int64_t)t * nsplit + split) * nhg + hg) * 4 + wave) *
+                              (VB_WAVE * 1024);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < VB_WAVE; ++db) {
       bf16x8 lo8, hi8;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
@@ -379,14 +338,14 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
       *(bf16x8*)(po + (db * 64 + lane) * 16 + 8) = hi8;
     }
   } else {
-    // final output: transpose the [64 heads x 512] block through LDS, then 16-byte stores
+    // final output: transpose the [32 heads x 512] block through LDS, then 16-byte stores
     __bf16* ot = (__bf16*)lds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int hl = hb * 32 + mfma32_row(r, lane);
+      const int hl = mfma32_row(r, lane);
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        ot[hl * DV + dvh * 256 + db * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
+      for (int db = 0; db < VB_WAVE; ++db)
+        ot[hl * DV + (VB_WAVE * cq + db) * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
     }
     __syncthreads();
     __bf16* ob = out + ((int64_t)t * H + hg * HG) * DV;
@@ -396,10 +355,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
       *(bf16x8*)(ob + piece * 8) = *(const bf16x8*)(ot + piece * 8);
     }
   }
-  if (kh == 0 && dvh == 0 && half == 0) {
-    const float l = fin[head_lane];
-    const float val = l > 0.f ? (fin[HG + head_lane] + log2f(l)) * kLn2 : -INFINITY;
-    const int64_t h = hg * HG + head_lane;
+  if (wave == 0 && half == 0) {
+    const float l = fin[c32];
+    const float val = l > 0.f ? (fin[HG + c32] + log2f(l)) * kLn2 : -INFINITY;
+    const int64_t h = hg * HG + c32;
     if (nsplit == 1) {
       if (lse) lse[(int64_t)t * H + h] = val;
     } else {
@@ -408,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16(
   }
 }
 
-// Merges the splits of one (query, head group, wave block, value block): 64 lanes, each with the
+// Merges the splits of one (query, 32-head group, wave, value block): 64 lanes, each with the
 // 16 (head, column) values the sparse kernel's accumulator layout gives it.
 // out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i (natural-log units).
 __global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ part_o,
@@ -418,13 +377,13 @@ __global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ par
   extern __shared__ float wgt[];               // [nsplit][32] merge weights per head
   const int t = blockIdx.x;
   const int y = blockIdx.y;
-  const int db = y & 7;
-  const int w = (y >> 3) & 3;
-  const int hg = y >> 5;
-  const int hb = w >> 1, dvh = w & 1;
+  const int db = y % VB_WAVE;
+  const int w = (y / VB_WAVE) % 4;
+  const int hg = y / (VB_WAVE * 4);
+  const int nhg = H / HG;
   const int lane = threadIdx.x;
-  const int h0 = hg * HG + hb * 32;            // first head of this block
-  // every split's log-sum-exp of the block's 32 heads, one coalesced load per lane and pass
+  const int h0 = hg * HG;                      // first head of this group
+  // every split's log-sum-exp of the group's 32 heads, one coalesced load per lane and pass
   for (int j = lane; j < nsplit * 32; j += 64)
     wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
   __syncthreads();
@@ -439,14 +398,14 @@ __global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ par
       const float li = wgt[i * 32 + lane];
       wgt[i * 32 + lane] = (li == -INFINITY) ? 0.f : expf(li - tot);
     }
-    if (lse && dvh == 0 && db == 0) lse[(int64_t)t * H + h0 + lane] = tot;
+    if (lse && w == 0 && db == 0) lse[(int64_t)t * H + h0 + lane] = tot;
   }
   __syncthreads();
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int64_t stride = (int64_t)(H / HG) * 4 * 8 * 1024;      // elements per (t, split)
-  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((hg * 4 + w) * 8 + db) * 1024 +
+  const int64_t stride = (int64_t)nhg * 4 * VB_WAVE * 1024;     // elements per (t, split)
+  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((hg * 4 + w) * VB_WAVE + db) * 1024 +
                      lane * 16;
   auto add = [&](int i, bf16x8 lo8, bf16x8 hi8) {
 #pragma unroll
@@ -468,8 +427,7 @@ __global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ par
   }
   for (; i < nsplit; ++i)
     add(i, *(const bf16x8*)(po + i * stride), *(const bf16x8*)(po + i * stride + 8));
-  __bf16* ob =
-      out + ((int64_t)t * H + hg * HG + hb * 32) * DV + dvh * 256 + db * 32 + (lane & 31);
+  __bf16* ob = out + ((int64_t)t * H + h0) * DV + (VB_WAVE * w + db) * 32 + (lane & 31);
 #pragma unroll
   for (int r = 0; r < 16; ++r) ob[(int64_t)mfma32_row(r, lane) * DV] = (__bf16)acc[r];
 }
@@ -542,7 +500,7 @@ MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
   const int tiles = (k + TILE - 1) / TILE;
   const int64_t wgs = (int64_t)b.total_q * (n_heads / HG);
   const int64_t wgs1 = wgs > 0 ? wgs : 1;
-  int nsplit = (int)((256 + wgs1 - 1) / wgs1);
+  int nsplit = (int)((512 + wgs1 - 1) / wgs1);          // two workgroups per CU
   nsplit = std::max(1, std::min(nsplit, (tiles + 1) / 2));          // at least 2 tiles per split
   const int tiles_per_split = (tiles + nsplit - 1) / nsplit;
   p.rows_per_split = tiles_per_split * TILE;
@@ -574,7 +532,7 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
       (__bf16*)out, lse, part_o, part_lse);
   e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 32), 64, plan.nsplit * 32 * sizeof(float),
+  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 4 * VB_WAVE), 64, plan.nsplit * 32 * sizeof(float),
                 stream>>>(part_o, part_lse, plan.nsplit, n_heads, (__bf16*)out, lse);
   return hipGetLastError();
 }

@@ -94,7 +94,7 @@ def test_sparse_mla_rejects_bad_arguments(L):
     assert f(*a) == INVALID
     a = list(args); a[7] = 600               # d_v > d_qk
     assert f(*a) == INVALID
-    a = list(args); a[5] = 48                # heads not a multiple of 64 on bf16
+    a = list(args); a[5] = 48                # heads not a multiple of 32 on bf16
     assert f(*a) == UNSUPPORTED
     a = list(args); a[6] = 512; a[7] = 448   # other latent widths are not compiled
     assert f(*a) == UNSUPPORTED
