@@ -9,9 +9,12 @@ bf16 latent rows). Inputs are seeded synthetic tensors resident in HBM before ti
 Steps rotate over several independent input sets whose total size exceeds the 256 MB
 Infinity Cache, so a step cannot be served from the previous step's cached lines.
 
+The timed steps launch their four kernels back to back on one stream (the GPU runs them without
+gaps); --launch graph replays one captured HIP graph per input set instead (slower here).
 Prints one JSON line: metric, value (query tokens/s), per-kernel times from HIP events on the
-launch stream inside the timed region, the roofline of the dominant kernel, and the CPU oracle
-timed on a bounded sample of the same workload.
+launch stream around every call of a second timed pass of the same steps launched kernel by
+kernel, the roofline of the dominant kernel, and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 import argparse
 import json
@@ -36,6 +39,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--launch", choices=["eager", "graph"], default="eager",
+                    help="time steps launched kernel by kernel (default) or replayed from one "
+                         "HIP graph per input set")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -166,6 +172,9 @@ def main():
     sp = stream.cuda_stream
 
     def step(i, ev=None):
+        step_on(i, sp, ev)
+
+    def step_on(i, sp, ev=None):
         d = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
@@ -191,13 +200,37 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    # --launch graph: one HIP graph per input set holds the step's kernels (same kernels, same
+    # arguments), replayed in the timed region.
+    graphs = []
+    if args.launch == "graph":
+        for i in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_on(i, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+        for i in range(max(2, nsets)):
+            graphs[i % nsets].replay()
+        torch.cuda.synchronize()
+
+    # timed region 1: the headline, K whole steps
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        if graphs:
+            graphs[(args.warmup + i) % nsets].replay()
+        else:
+            step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+
+    # timed region 2: the same K steps launched kernel by kernel, with HIP events on the launch
+    # stream around every call (per-kernel durations and the roofline)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
     ms_idx = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     ms_topk = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms_mla = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
@@ -235,7 +268,8 @@ def main():
                                f"{case.index_head_dim}, top-{case.index_topk}, "
                                f"{case.n_heads}-head MQA over {case.d_qk}-wide latent "
                                f"({case.d_v} value), {case.layers} layer(s) per index pass",
-                   "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets},
+                   "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets,
+                   "launch": "hip_graph" if graphs else "eager"},
         "achieved_hbm_gbps": round(sb / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": sb,
         "kernel_ms": {"indexer": round(ms_idx, 5), "topk": round(ms_topk, 5),
