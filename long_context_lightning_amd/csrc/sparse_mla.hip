@@ -168,6 +168,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
       }
     };
 
+    // the first tile's gathers go out as soon as its indices arrive; the query block loads
+    // behind them and both are waited for at the top of the first tile
+    int idx_cur = load_idx(0);
+    wait_all_memory();
+    issue(idx_cur);
     bf16x8 qreg[QK_STEPS];
     {
       const __bf16* qr = q + ((int64_t)t * H + hg * HG + c32) * DQK + kh * (QK_STEPS * 16) +
@@ -175,9 +180,6 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
 #pragma unroll
       for (int i = 0; i < QK_STEPS; ++i) qreg[i] = *(const bf16x8*)(qr + i * 16);
     }
-    int idx_cur = load_idx(0);
-    wait_all_memory();
-    issue(idx_cur);
     // A-operand lane bases: step i reads chunk 36*kh + 2*i + half of row 32*rb + c32; with
     // u = 2*kh + i the slot is 8*(4*kh + u/4) + ((2*(u%4) + half) ^ swz): four lane bases plus
     // 128*(i/4) immediates.

@@ -6,7 +6,7 @@
 // Scores are finite or infinite; a NaN score is never selected.
 //
 // One workgroup of 1024 threads per query row; the scores stay in registers:
-//   * the row is cut into chunks of UNITS*4096 positions (UNITS <= 4); inside a chunk, wave w
+//   * the row is cut into chunks of UNITS*4096 positions (UNITS <= 8); inside a chunk, wave w
 //     owns a contiguous slice and lane l of it holds UNITS 16-byte groups, (u*64 + l) within it.
 //     A row of at most one chunk is read from memory once; longer rows re-read their chunks on
 //     every pass. Slots outside the row hold NaN, which no comparison or bin counts;
@@ -390,12 +390,13 @@ size_t topk_workspace_bytes(const Batch&, int) { return 0; }
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        void*, hipStream_t stream) {
   // Registers per thread sized for the longest visible row (16-byte groups, plus one for a row
-  // that does not start on a 16-byte boundary); rows longer than 16K keys are processed in chunks.
+  // that does not start on a 16-byte boundary); rows longer than 32K keys are processed in chunks.
   const int64_t longest = std::min<int64_t>(b.max_k, ld);
   const int64_t groups = (longest + 3) / 4 + 1;
   if (groups <= 1 * TK_THREADS) return launch_rows<1>(b, scores, ld, k, indices, stream);
   if (groups <= 2 * TK_THREADS) return launch_rows<2>(b, scores, ld, k, indices, stream);
-  return launch_rows<4>(b, scores, ld, k, indices, stream);
+  if (groups <= 4 * TK_THREADS) return launch_rows<4>(b, scores, ld, k, indices, stream);
+  return launch_rows<8>(b, scores, ld, k, indices, stream);
 }
 
 }  // namespace dsa
