@@ -91,7 +91,10 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
  * positions are written in ascending order.
  *   scores  [T, ld_scores] fp32 (only s <= p is read)
  *   indices [T, index_topk] int32, sequence-local positions
- *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 bytes / NULL when that is 0)
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 bytes / NULL when that is 0).
+ *     It is non-zero for batches of at most 64 query rows whose longest sequence exceeds 32768
+ *     keys: those rows are split over several workgroups that meet through per-row histograms
+ *     and counts kept there. Its contents on entry do not matter; on return they are undefined.
  * Scores must not be NaN. */
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
                     int32_t index_topk, int32_t* indices, void* workspace, size_t ws_bytes,

@@ -5,7 +5,9 @@
 // (-0.0 == +0.0), an equal score going to the lower position; output ascending, -1 padded.
 // Scores are finite or infinite; a NaN score is never selected.
 //
-// One workgroup of 1024 threads per query row; the scores stay in registers:
+// Batches of many rows (prefill, wide decode) use one workgroup of 1024 threads per query row,
+// described here; batches of a few long rows split each row over several workgroups (further
+// down). With one workgroup per row the scores stay in registers:
 //   * the row is cut into chunks of UNITS*4096 positions (UNITS <= 8); inside a chunk, wave w
 //     owns a contiguous slice and lane l of it holds UNITS 16-byte groups, (u*64 + l) within it.
 //     A row of at most one chunk is read from memory once; longer rows re-read their chunks on
@@ -375,6 +377,636 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   });
 }
 
+// ---------------------------------------------------------------------------------------------
+// Rows split over several workgroups. A batch of a few long rows (long-context decode) leaves
+// most compute units idle under one workgroup per row, so each row is cut into chunks of
+// SP_CHUNK positions, one 256-thread workgroup per chunk with the chunk in registers, and the
+// select runs as five launches that meet through per-row counters in the workspace:
+//   prep     chunk minimum / maximum; clears the row's histograms
+//   hist0    2048 bins linear between the row's smallest and largest score (bins of a
+//            power-of-two key width when that range is not finite), added into the row's
+//            histogram with one global atomic per non-empty bin
+//   hist1    the bin holding the k-th largest score split into 2048 finer bins, with each
+//            bin's smallest and largest key
+//   count    per chunk, the scores above the chosen fine bin and inside it; when the chosen
+//            bin neither holds one value nor is taken whole, the positions inside it are
+//            appended to a per-row candidate list
+//   compact  every workgroup resolves the threshold (from the candidates when needed, in key
+//            space), sums the counts of the chunks before its own and writes its selected
+//            positions in index order.
+// Every workgroup of a row derives the same bins from the same global values, so the five
+// launches agree on every decision without a grid-wide barrier.
+// ---------------------------------------------------------------------------------------------
+constexpr int SP_THREADS = 256;
+constexpr int SP_WAVES = SP_THREADS / WAVE;
+constexpr int SP_UNITS = 8;
+constexpr int SP_SLICE4 = SP_UNITS * WAVE;          // 16-byte groups per wave and chunk
+constexpr int SP_CHUNK4 = SP_UNITS * SP_THREADS;    // 16-byte groups per chunk (8192 positions)
+constexpr int SP_BPT = TK_BINS / SP_THREADS;        // bins per thread in a select
+
+// Per-row words of the workspace.
+constexpr int RW_HIST0 = 0;
+constexpr int RW_HIST1 = TK_BINS;
+constexpr int RW_MIN1 = 2 * TK_BINS;
+constexpr int RW_MAX1 = 3 * TK_BINS;
+constexpr int RW_CAND_N = 4 * TK_BINS;
+constexpr int RW_WORDS = 4 * TK_BINS + 64;
+
+struct SplitWs {
+  uint32_t* rows;      // [total_q][RW_WORDS]
+  float2* minmax;      // [total_q][max_chunks]  chunk min / max score
+  uint2* counts;       // [total_q][max_chunks]  chunk (above, inside) the chosen fine bin
+  uint32_t* cand;      // [total_q][cand_cap]    positions inside the chosen fine bin
+  int max_chunks;
+  int max_k;
+  int64_t cand_cap;
+};
+
+struct SplitShared {
+  uint32_t hist[TK_BINS];
+  uint32_t bmin[TK_BINS];
+  uint32_t bmax[TK_BINS];
+  uint32_t red_a[SP_WAVES], red_b[SP_WAVES], red_c[SP_WAVES], red_d[SP_WAVES];
+  uint32_t sel_bin, sel_need, sel_count, sel_min, sel_max, bcast;
+};
+
+// Row t, chunk c of this workgroup and the chunk's place in the score row.
+struct SplitChunk {
+  int t, c;
+  int ni;                 // visible positions 0..ni-1
+  int off, ng4, nchunks;  // the row is read in aligned 16-byte groups; `off` floats precede it
+  bool dense;             // ni <= k: everything visible is selected
+  const float* srow;
+  const f32x4* g4;
+};
+
+__device__ __forceinline__ SplitChunk split_chunk(const float* scores, int64_t ld,
+                                                  const int32_t* cu_q, const int64_t* cu_k,
+                                                  int nseq, int64_t total_k, int k,
+                                                  int max_k, int max_chunks) {
+  SplitChunk r;
+  r.t = blockIdx.x / max_chunks;
+  r.c = blockIdx.x - r.t * max_chunks;
+  const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, r.t);
+  // a row is never longer than the batch's longest sequence, which sized the workspace
+  const int64_t n = min(min(qp.p + 1, ld), (int64_t)max_k);
+  r.ni = (int)max((int64_t)0, n);
+  r.dense = n <= k;
+  r.srow = scores + (int64_t)r.t * ld;
+  r.off = (int)((reinterpret_cast<uintptr_t>(r.srow) >> 2) & 3);
+  r.g4 = reinterpret_cast<const f32x4*>(r.srow - r.off);
+  r.ng4 = (r.ni + r.off + 3) >> 2;
+  r.nchunks = (r.ng4 + SP_CHUNK4 - 1) / SP_CHUNK4;
+  return r;
+}
+
+// Unit u of this lane is group c*SP_CHUNK4 + wave*SP_SLICE4 + 64*u + lane; its element e is
+// position 4*group + e - off. Slots outside the row hold NaN.
+__device__ __forceinline__ void split_load(const SplitChunk& r, float (&x)[SP_UNITS][4]) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const float qnan = __uint_as_float(0x7fc00000u);
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u) {
+    const int g = r.c * SP_CHUNK4 + wave * SP_SLICE4 + u * WAVE + lane;
+    f32x4 v = {qnan, qnan, qnan, qnan};
+    if (g < r.ng4) v = r.g4[g];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[u][e] = v[e];
+    if (g == 0 || g == r.ng4 - 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = 4 * g + e - r.off;
+        if (pos < 0 || pos >= r.ni) x[u][e] = qnan;
+      }
+    }
+  }
+}
+
+// Workgroup-wide min and max (NaN ignored). Two barriers.
+__device__ __forceinline__ void wg_minmax(float& mn, float& mx, SplitShared& sh) {
+  const int wave = threadIdx.x >> 6;
+  mn = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(mn), 0x7f800000u, MinF32())));
+  mx = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(mx), 0xff800000u, MaxF32())));
+  if (lane_id() == 0) { sh.red_a[wave] = __float_as_uint(mn); sh.red_b[wave] = __float_as_uint(mx); }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < SP_WAVES; ++w) {
+    mn = fminf(mn, __uint_as_float(sh.red_a[w]));
+    mx = fmaxf(mx, __uint_as_float(sh.red_b[w]));
+  }
+  __syncthreads();
+}
+
+// Workgroup-wide sums of two counts. Two barriers.
+__device__ __forceinline__ void wg_sum2(uint32_t& a, uint32_t& b, SplitShared& sh) {
+  const int wave = threadIdx.x >> 6;
+  a = last_lane(wave_incl_scan_u32(a));
+  b = last_lane(wave_incl_scan_u32(b));
+  if (lane_id() == 0) { sh.red_c[wave] = a; sh.red_d[wave] = b; }
+  __syncthreads();
+  a = 0;
+  b = 0;
+#pragma unroll
+  for (int w = 0; w < SP_WAVES; ++w) { a += sh.red_c[w]; b += sh.red_d[w]; }
+  __syncthreads();
+}
+
+// In histogram h (global or LDS; SP_BPT consecutive bins per thread, keys counted from the top
+// bin down), finds the bin holding the need-th largest key and publishes it with the keys
+// still needed from it, its count and, when mn / mx are given, its smallest and largest key.
+// If the histogram holds fewer than `need` keys, sel_count is 0. Three barriers (the first one
+// lets every thread finish reading the previous select's results).
+__device__ __forceinline__ void split_select(const uint32_t* h, const uint32_t* mn,
+                                             const uint32_t* mx, uint32_t need,
+                                             SplitShared& sh) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  uint32_t hv[SP_BPT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < SP_BPT; ++j) {
+    hv[j] = h[SP_BPT * tid + j];
+    s += hv[j];
+  }
+  const uint32_t incl = wave_incl_scan_u32(s);
+  const uint32_t wave_tot = last_lane(incl);
+  if (lane_id() == 0) sh.red_a[wave] = wave_tot;
+  if (tid == 0) { sh.sel_bin = 0; sh.sel_need = need; sh.sel_count = 0; sh.sel_min = 0; sh.sel_max = 0; }
+  __syncthreads();
+  uint32_t above = wave_tot - incl;              // keys in bins above this thread's bins
+#pragma unroll
+  for (int w = 0; w < SP_WAVES; ++w)
+    if (w > wave) above += sh.red_a[w];
+#pragma unroll
+  for (int j = SP_BPT - 1; j >= 0; --j) {
+    if (above < need && above + hv[j] >= need) {
+      const int b = SP_BPT * tid + j;
+      sh.sel_bin = b;
+      sh.sel_need = need - above;
+      sh.sel_count = hv[j];
+      sh.sel_min = mn ? mn[b] : 0u;
+      sh.sel_max = mx ? mx[b] : 0u;
+    }
+    above += hv[j];
+  }
+  __syncthreads();
+}
+
+// Bins of the first two rounds of a row, from its smallest and largest score (every workgroup of
+// the row computes the same values).
+struct SplitBins {
+  int mode;               // 0: one value (or none), 1: linear bins, 2: key bins
+  float xmin, xmax;
+  float s0, c0;           // linear round 0
+  uint32_t lo0;           // key round 0: bin = (key - lo0) >> shift0
+  int shift0;
+};
+
+__device__ __forceinline__ SplitBins split_bins(const float2* mm, int nchunks, SplitShared& sh) {
+  float mn = __int_as_float(0x7f800000), mx = -mn;
+  for (int i = threadIdx.x; i < nchunks; i += SP_THREADS) {
+    const float2 v = mm[i];
+    mn = fminf(mn, v.x);
+    mx = fmaxf(mx, v.y);
+  }
+  wg_minmax(mn, mx, sh);
+  SplitBins sb;
+  sb.xmin = mn;
+  sb.xmax = mx;
+  sb.s0 = 0.f;
+  sb.c0 = 0.f;
+  sb.lo0 = 0;
+  sb.shift0 = 0;
+  if (!(mn < mx)) {
+    sb.mode = 0;
+    return sb;
+  }
+  const float s0 = (float)TK_BINS / (mx - mn);
+  if (s0 > 0.f && s0 <= __FLT_MAX__) {
+    sb.mode = 1;
+    sb.s0 = s0;
+    sb.c0 = -mn * s0;
+  } else {
+    sb.mode = 2;
+    sb.lo0 = score_key(mn);
+    const uint32_t span = score_key(mx) - sb.lo0;
+    int shift = 0;
+    while ((span >> shift) >= (uint32_t)TK_BINS) ++shift;
+    sb.shift0 = shift;
+  }
+  return sb;
+}
+
+__device__ __forceinline__ uint32_t split_bin0(const SplitBins& sb, float v) {
+  if (sb.mode == 1) return lin_bin(v, sb.s0, sb.c0);
+  return v == v ? (score_key(v) - sb.lo0) >> sb.shift0 : (uint32_t)TK_BINS;
+}
+
+// Fine bins inside round-0 bin `bin0`.
+struct SplitBins1 {
+  float s1, c1;
+  uint32_t base1;
+  int shift1;
+};
+
+__device__ __forceinline__ SplitBins1 split_bins1(const SplitBins& sb, uint32_t bin0) {
+  SplitBins1 b1;
+  b1.s1 = 0.f;
+  b1.c1 = 0.f;
+  b1.base1 = 0;
+  b1.shift1 = 0;
+  if (sb.mode == 1) {
+    float s1 = sb.s0 * (float)TK_BINS;
+    float c1 = -(sb.xmin + (float)bin0 / sb.s0) * s1;
+    if (!(s1 <= __FLT_MAX__ && c1 <= __FLT_MAX__ && c1 >= -__FLT_MAX__)) { s1 = 0.f; c1 = 0.f; }
+    b1.s1 = s1;
+    b1.c1 = c1;
+  } else {
+    b1.base1 = sb.lo0 + (bin0 << sb.shift0);
+    b1.shift1 = sb.shift0 > 11 ? sb.shift0 - 11 : 0;
+  }
+  return b1;
+}
+
+__device__ __forceinline__ uint32_t split_bin1(const SplitBins& sb, const SplitBins1& b1, float v) {
+  if (sb.mode == 1) return lin_bin(v, b1.s1, b1.c1);
+  return (score_key(v) - b1.base1) >> b1.shift1;
+}
+
+// The chosen fine bin: keys [lo, hi] of which `need` are taken, `count` keys inside it.
+struct SplitChoice {
+  uint32_t lo, hi, count, need;
+};
+
+__device__ __forceinline__ SplitChoice split_choice(const SplitBins& sb, const uint32_t* rw, int k,
+                                                    SplitShared& sh) {
+  SplitChoice ch;
+  if (sb.mode == 0) {                            // one value: take the first k of them
+    ch.lo = ch.hi = score_key(sb.xmin);
+    ch.count = 0xffffffffu;
+    ch.need = (uint32_t)k;
+    return ch;
+  }
+  split_select(rw + RW_HIST0, nullptr, nullptr, (uint32_t)k, sh);
+  const uint32_t need1 = sh.sel_need;
+  split_select(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, need1, sh);
+  ch.lo = sh.sel_min;
+  ch.hi = sh.sel_max;
+  ch.count = sh.sel_count;
+  ch.need = sh.sel_need;
+  return ch;
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_prep(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  if (r.dense || r.c >= r.nchunks) return;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  for (int i = r.c * SP_THREADS + threadIdx.x; i < RW_WORDS; i += r.nchunks * SP_THREADS)
+    rw[i] = (i >= RW_MIN1 && i < RW_MAX1) ? 0xffffffffu : 0u;
+  float mn = __int_as_float(0x7f800000), mx = -mn;
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn = fminf(mn, x[u][e]);
+      mx = fmaxf(mx, x[u][e]);
+    }
+  wg_minmax(mn, mx, sh);
+  if (threadIdx.x == 0) ws.minmax[(int64_t)r.t * ws.max_chunks + r.c] = make_float2(mn, mx);
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_hist0(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  if (r.dense || r.c >= r.nchunks) return;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) sh.hist[i] = 0;
+  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  if (sb.mode == 0) return;
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b = split_bin0(sb, x[u][e]);
+      if (b < (uint32_t)TK_BINS) atomicAdd(&sh.hist[b], 1u);
+    }
+  __syncthreads();
+  uint32_t* hg = ws.rows + (int64_t)r.t * RW_WORDS + RW_HIST0;
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS)
+    if (sh.hist[i]) atomicAdd(&hg[i], sh.hist[i]);
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_hist1(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  if (r.dense || r.c >= r.nchunks) return;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) {
+    sh.hist[i] = 0;
+    sh.bmin[i] = 0xffffffffu;
+    sh.bmax[i] = 0u;
+  }
+  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  if (sb.mode == 0) return;
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  split_select(rw + RW_HIST0, nullptr, nullptr, (uint32_t)k, sh);
+  const uint32_t bin0 = sh.sel_bin;
+  const SplitBins1 b1 = split_bins1(sb, bin0);
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = x[u][e];
+      if (split_bin0(sb, v) == bin0) {
+        const uint32_t b = split_bin1(sb, b1, v);
+        const uint32_t kk = score_key(v);
+        atomicAdd(&sh.hist[b], 1u);
+        atomicMin(&sh.bmin[b], kk);
+        atomicMax(&sh.bmax[b], kk);
+      }
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) {
+    const uint32_t h = sh.hist[i];
+    if (h) {
+      atomicAdd(&rw[RW_HIST1 + i], h);
+      atomicMin(&rw[RW_MIN1 + i], sh.bmin[i]);
+      atomicMax(&rw[RW_MAX1 + i], sh.bmax[i]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_count(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  if (r.dense || r.c >= r.nchunks) return;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const SplitChoice ch = split_choice(sb, rw, k, sh);
+  const float vlo = key_value(ch.lo), vhi = key_value(ch.hi);
+  uint32_t above = 0, inside = 0;
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = x[u][e];
+      above += v > vhi;
+      inside += v >= vlo && v <= vhi;
+    }
+  const uint32_t mine = inside;
+  wg_sum2(above, inside, sh);
+  if (threadIdx.x == 0) ws.counts[(int64_t)r.t * ws.max_chunks + r.c] = make_uint2(above, inside);
+  if (ch.count == ch.need || ch.lo == ch.hi || inside == 0) return;
+  // unresolved: append this chunk's positions inside [lo, hi] to the row's candidate list
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan_u32(mine);
+  if (lane_id() == WAVE - 1) sh.red_a[wave] = incl;
+  if (threadIdx.x == 0) sh.bcast = atomicAdd(&rw[RW_CAND_N], inside);
+  __syncthreads();
+  uint32_t slot = sh.bcast + incl - mine;
+  for (int w = 0; w < wave; ++w) slot += sh.red_a[w];
+  uint32_t* cand = ws.cand + (int64_t)r.t * ws.cand_cap;
+  const int g0 = r.c * SP_CHUNK4 + wave * SP_SLICE4 + lane_id();
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = x[u][e];
+      if (v >= vlo && v <= vhi) {
+        if (slot < ws.cand_cap) cand[slot] = (uint32_t)(4 * (g0 + u * WAVE) + e - r.off);
+        ++slot;
+      }
+    }
+}
+
+// Threshold among the candidates (keys [lo, hi], `count` of them, `need` to take), in rounds of
+// 2048 key bins of a power-of-two width: the score T and how many scores equal to T are taken
+// (all of them when thr_need is 0xffffffff).
+__device__ __forceinline__ void split_resolve_candidates(const float* srow, const uint32_t* cand,
+                                                         uint32_t ncand, SplitChoice ch,
+                                                         float& thr, uint32_t& thr_need,
+                                                         SplitShared& sh) {
+  uint32_t lo = ch.lo, hi = ch.hi, count = ch.count, need = ch.need;
+  for (;;) {
+    if (count == need) { thr = key_value(lo); thr_need = 0xffffffffu; return; }
+    if (lo == hi || count == 0) { thr = key_value(lo); thr_need = need; return; }
+    const uint32_t span = hi - lo;
+    int shift = 0;
+    while ((span >> shift) >= (uint32_t)TK_BINS) ++shift;
+    for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) {
+      sh.hist[i] = 0;
+      sh.bmin[i] = 0xffffffffu;
+      sh.bmax[i] = 0u;
+    }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
+      const uint32_t kk = score_key(srow[cand[i]]);
+      if (kk >= lo && kk <= hi) {
+        const uint32_t b = (kk - lo) >> shift;
+        atomicAdd(&sh.hist[b], 1u);
+        atomicMin(&sh.bmin[b], kk);
+        atomicMax(&sh.bmax[b], kk);
+      }
+    }
+    __syncthreads();
+    split_select(sh.hist, sh.bmin, sh.bmax, need, sh);
+    count = sh.sel_count;
+    need = sh.sel_need;
+    lo = sh.sel_min;
+    hi = sh.sel_max;
+    __syncthreads();                             // hist is cleared by the next round
+  }
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws,
+    int32_t* __restrict__ out) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  int32_t* orow = out + (int64_t)r.t * k;
+  if (r.dense) {
+    if (r.c == 0)
+      for (int i = threadIdx.x; i < k; i += SP_THREADS) orow[i] = i < r.ni ? i : -1;
+    return;
+  }
+  if (r.c >= r.nchunks) return;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  const uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const SplitChoice ch = split_choice(sb, rw, k, sh);
+  // counts of the chunks before this one
+  uint32_t above_b = 0, inside_b = 0;
+  const uint2* cnt = ws.counts + (int64_t)r.t * ws.max_chunks;
+  for (int i = threadIdx.x; i < r.c; i += SP_THREADS) {
+    const uint2 v = cnt[i];
+    above_b += v.x;
+    inside_b += v.y;
+  }
+  wg_sum2(above_b, inside_b, sh);
+  float thr;
+  uint32_t thr_need, gt_before, eq_before;
+  if (ch.count == ch.need) {                     // the whole fine bin is taken
+    thr = key_value(ch.lo);
+    thr_need = 0xffffffffu;
+    gt_before = above_b + inside_b;
+    eq_before = 0;
+  } else if (ch.lo == ch.hi) {                   // one value: the first `need` of it are taken
+    thr = key_value(ch.lo);
+    thr_need = ch.need;
+    gt_before = above_b;
+    eq_before = inside_b;
+  } else {
+    const uint32_t* cand = ws.cand + (int64_t)r.t * ws.cand_cap;
+    const uint32_t ncand = (uint32_t)min((int64_t)rw[RW_CAND_N], ws.cand_cap);
+    split_resolve_candidates(r.srow, cand, ncand, ch, thr, thr_need, sh);
+    const int first_pos = 4 * r.c * SP_CHUNK4 - r.off;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
+      const uint32_t pos = cand[i];
+      if ((int)pos < first_pos) {
+        const float v = r.srow[pos];
+        gt += v > thr;
+        eq += v == thr;
+      }
+    }
+    wg_sum2(gt, eq, sh);
+    gt_before = above_b + gt;
+    eq_before = eq;
+  }
+
+  // compaction of this chunk in index order
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gt += (uint32_t)__popcll(__ballot(x[u][e] > thr));
+      eq += (uint32_t)__popcll(__ballot(x[u][e] == thr));
+    }
+  if (lane == 0) { sh.red_c[wave] = gt; sh.red_d[wave] = eq; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < SP_WAVES; ++w)
+    if (w < wave) { gt_before += sh.red_c[w]; eq_before += sh.red_d[w]; }
+  uint32_t eqc = eq_before;
+  uint32_t base = gt_before + min(eq_before, thr_need);
+  const int g0 = r.c * SP_CHUNK4 + wave * SP_SLICE4 + lane;
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u) {
+    uint64_t tm[4];
+    uint64_t eq_any = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tm[e] = __ballot(x[u][e] > thr);
+      eq_any |= __ballot(x[u][e] == thr);
+    }
+    if (eq_any) {
+      uint64_t qm[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qm[e] = __ballot(x[u][e] == thr);
+      uint32_t rank = eqc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rank += lanes_below(qm[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool is_eq = x[u][e] == thr;
+        tm[e] |= __ballot(is_eq && rank < thr_need);
+        rank += is_eq;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eqc += (uint32_t)__popcll(qm[e]);
+    }
+    uint32_t slot = base;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) slot += lanes_below(tm[e]);
+    const int p0 = 4 * (g0 + u * WAVE) - r.off;
+    const uint64_t lane_bit = 1ull << lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (tm[e] & lane_bit) {
+        if (slot < (uint32_t)k) orow[slot] = p0 + e;
+        ++slot;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) base += (uint32_t)__popcll(tm[e]);
+  }
+}
+
+// Layout of the split workspace for this batch; rows.. cand are null when ws is null.
+struct SplitLayout {
+  int max_chunks;
+  int64_t cand_cap;
+  size_t rows_off, minmax_off, counts_off, cand_off, bytes;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+SplitLayout split_layout(const Batch& b) {
+  SplitLayout L;
+  const int64_t groups = ((int64_t)b.max_k + 3) / 4 + 1;
+  L.max_chunks = (int)((groups + SP_CHUNK4 - 1) / SP_CHUNK4);
+  L.cand_cap = ((int64_t)b.max_k + 63) & ~(int64_t)63;
+  const size_t T = (size_t)b.total_q;
+  L.rows_off = 0;
+  L.minmax_off = align256(T * RW_WORDS * sizeof(uint32_t));
+  L.counts_off = L.minmax_off + align256(T * L.max_chunks * sizeof(float2));
+  L.cand_off = L.counts_off + align256(T * L.max_chunks * sizeof(uint2));
+  L.bytes = L.cand_off + align256(T * (size_t)L.cand_cap * sizeof(uint32_t));
+  return L;
+}
+
+// Split rows when the batch has too few rows to fill the chip with one workgroup per row and
+// the rows are longer than one register-resident chunk of the single-workgroup kernel.
+bool use_split(const Batch& b, int k) {
+  return b.max_k > 4 * TK_THREADS * 8 && b.max_k > k && b.total_q <= 64;
+}
+
+hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
+                        void* workspace, hipStream_t stream) {
+  const SplitLayout L = split_layout(b);
+  char* base = (char*)workspace;
+  SplitWs ws;
+  ws.rows = (uint32_t*)(base + L.rows_off);
+  ws.minmax = (float2*)(base + L.minmax_off);
+  ws.counts = (uint2*)(base + L.counts_off);
+  ws.cand = (uint32_t*)(base + L.cand_off);
+  ws.max_chunks = L.max_chunks;
+  ws.max_k = b.max_k;
+  ws.cand_cap = L.cand_cap;
+  const unsigned grid = (unsigned)((int64_t)b.total_q * L.max_chunks);
+  topk_split_prep<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq, b.total_k,
+                                                   k, ws);
+  topk_split_hist0<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
+                                                    b.total_k, k, ws);
+  topk_split_hist1<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
+                                                    b.total_k, k, ws);
+  topk_split_count<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
+                                                    b.total_k, k, ws);
+  topk_split_compact<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
+                                                      b.total_k, k, ws, indices);
+  return hipGetLastError();
+}
+
 template <int UNITS>
 hipError_t launch_rows(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        hipStream_t stream) {
@@ -385,10 +1017,13 @@ hipError_t launch_rows(const Batch& b, const float* scores, int64_t ld, int k, i
 
 }  // namespace
 
-size_t topk_workspace_bytes(const Batch&, int) { return 0; }
+size_t topk_workspace_bytes(const Batch& b, int k) {
+  return use_split(b, k) ? split_layout(b).bytes : 0;
+}
 
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
-                       void*, hipStream_t stream) {
+                       void* workspace, hipStream_t stream) {
+  if (use_split(b, k)) return launch_split(b, scores, ld, k, indices, workspace, stream);
   // Registers per thread sized for the longest visible row (16-byte groups, plus one for a row
   // that does not start on a 16-byte boundary); rows longer than 32K keys are processed in chunks.
   const int64_t longest = std::min<int64_t>(b.max_k, ld);

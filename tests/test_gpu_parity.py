@@ -398,8 +398,36 @@ def test_topk_crafted_rows():
     big = rng.integers(-3, 4, 300000).astype(np.float32)        # long row, huge tie groups
     rows.append(big)
     rows.append(np.array([np.inf, -np.inf, 1.0, 3.0e38, -3.0e38] * 1000, dtype=np.float32))
+    # one outlier stretches the linear bins so far that both linear rounds put every other
+    # score into one fine bin: the threshold is found among the listed candidates
+    out = (1.0 + rng.random(100000) * 1e-3).astype(np.float32)
+    out[77777] = 1e30
+    rows.append(out)
+    # candidates with large tie groups straddling the k-th score
+    tie = np.round(rng.random(90000) * 50).astype(np.float32) * np.float32(1e-6) + np.float32(1.0)
+    tie[12345] = -1e30
+    rows.append(tie)
     _crafted_topk(rows, 2048)
     _crafted_topk([r[:5000] for r in rows], 7)
+
+
+def test_topk_many_long_rows():
+    """More rows than the split-row path takes: one workgroup per row, the row in chunks."""
+    rng = np.random.default_rng(9)
+    rows = [rng.integers(-6, 7, int(n)).astype(np.float32)
+            for n in rng.integers(33000, 70000, 72)]
+    rows[3] = rng.normal(size=rows[3].shape[0]).astype(np.float32)
+    _crafted_topk(rows, 2048)
+
+
+def test_topk_split_rows_mixed_lengths():
+    """A few long rows with short and dense rows beside them (the split-row path)."""
+    rng = np.random.default_rng(10)
+    lens = [1000, 2048, 2049, 8191, 8192, 8193, 40000, 131075, 300001]
+    rows = [rng.normal(size=n).astype(np.float32) for n in lens]
+    rows[7] = rng.integers(-4, 5, lens[7]).astype(np.float32)
+    _crafted_topk(rows, 2048)
+    _crafted_topk(rows, 6000)
 
 
 def test_reference_max_restart_path():
