@@ -222,7 +222,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 #pragma unroll
         for (int u = 0; u < UNITS; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[0][lin_bin(x[u][e], s0, c0)], 1u);
+          for (int e = 0; e < 4; ++e)
+            if (x[u][e] == x[u][e]) atomicAdd(&sh.hist[0][lin_bin(x[u][e], s0, c0)], 1u);
       });
       __syncthreads();
       select_bin(sh.hist[0], sh.bmin[0], sh.bmax[0], need, sh);
@@ -1024,10 +1025,11 @@ size_t topk_workspace_bytes(const Batch& b, int k) {
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        void* workspace, hipStream_t stream) {
   if (use_split(b, k)) return launch_split(b, scores, ld, k, indices, workspace, stream);
-  // Registers per thread sized for the longest visible row (16-byte groups, plus one for a row
-  // that does not start on a 16-byte boundary); rows longer than 32K keys are processed in chunks.
+  // Registers per thread sized for the longest visible row (16-byte groups, plus one when rows
+  // do not all start on a 16-byte boundary); rows longer than 32K keys are processed in chunks.
   const int64_t longest = std::min<int64_t>(b.max_k, ld);
-  const int64_t groups = (longest + 3) / 4 + 1;
+  const bool aligned = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && ld % 4 == 0;
+  const int64_t groups = (longest + 3) / 4 + (aligned ? 0 : 1);
   if (groups <= 1 * TK_THREADS) return launch_rows<1>(b, scores, ld, k, indices, stream);
   if (groups <= 2 * TK_THREADS) return launch_rows<2>(b, scores, ld, k, indices, stream);
   if (groups <= 4 * TK_THREADS) return launch_rows<4>(b, scores, ld, k, indices, stream);
