@@ -54,6 +54,14 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_wave
 // Wait for every outstanding vector-memory, LDS and export operation of this wave.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete in
+// issue order, so every older one has landed); LDS and export counters are not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Order-preserving unsigned key of a float score: a > b (as reals) <=> key(a) > key(b).
 // -0.0 and +0.0 are the same real number and get the same key.
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -155,20 +163,51 @@ struct QueryPos {
   int64_t len;      // L_b
 };
 
-// t must be the same for all 64 lanes of the wave (the lookup is a wave-wide ballot).
+// t must be the same for all 64 lanes of the wave (the lookup is a wave-wide ballot). One memory
+// round trip per 64 sequences: lane j loads both boundaries of sequence base+j from cu_q and cu_k
+// together (index clamped into the arrays, so the loads are unconditional), the ballot over cu_q
+// finds the sequence, and its boundaries are read from that lane. The first 64 sequences are
+// looked up outside the loop, so the compiler adds no wait there for loads issued before.
+__device__ __forceinline__ bool query_pos_step(const int32_t* __restrict__ cu_q,
+                                               const int64_t* __restrict__ cu_k, int nseq, int t,
+                                               int base, int64_t (&v)[5]) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int j = min(base + lane, max(nseq - 1, 0));
+  int32_t qa = cu_q[j], qb = cu_q[j + 1];
+  int64_t ka = cu_k[j], kb = cu_k[j + 1];
+  // all four loads are issued before the ballot (the compiler would otherwise sink three of them
+  // behind it, into a second round trip)
+  asm volatile("" : "+v"(qa), "+v"(qb), "+v"(ka), "+v"(kb));
+  const bool le = base + lane + 1 < nseq && qb <= t;   // sequence base+lane+1 starts at or before t
+  const int cnt = __popcll(__ballot(le));
+  if (cnt == WAVE) return false;
+  auto rd64 = [&](int64_t x) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), cnt) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)x, cnt));
+  };
+  v[0] = base + cnt;
+  v[1] = __builtin_amdgcn_readlane(qa, cnt);
+  v[2] = __builtin_amdgcn_readlane(qb, cnt);
+  v[3] = rd64(ka);
+  v[4] = rd64(kb);
+  return true;
+}
+
 __device__ __forceinline__ QueryPos query_pos(const int32_t* __restrict__ cu_q,
                                               const int64_t* __restrict__ cu_k, int nseq,
                                               int64_t total_k, int t) {
+  int64_t v[5];                                // b, cu_q[b], cu_q[b+1], cu_k[b], cu_k[b+1]
+  if (!query_pos_step(cu_q, cu_k, nseq, t, 0, v))
+    for (int base = WAVE;; base += WAVE)
+      if (query_pos_step(cu_q, cu_k, nseq, t, base, v)) break;
   QueryPos r;
-  r.b = find_seq_wave(cu_q, nseq, t);
-  int64_t q0 = cu_q[r.b], q1 = cu_q[r.b + 1];
-  int64_t k0 = cu_k[r.b], k1 = cu_k[r.b + 1];
-  k0 = max((int64_t)0, min(k0, total_k));
-  k1 = max(k0, min(k1, total_k));
+  r.b = (int)v[0];
+  int64_t k0 = max((int64_t)0, min(v[3], total_k));
+  int64_t k1 = max(k0, min(v[4], total_k));
   r.key_base = k0;
   r.len = k1 - k0;
-  int64_t nq = q1 - q0;
-  r.p = (t >= q0 && t < q1) ? r.len - nq + (t - q0) : -1;
+  const int64_t nq = v[2] - v[1];
+  r.p = (t >= v[1] && t < v[2]) ? r.len - nq + (t - v[1]) : -1;
   if (r.p >= r.len) r.p = r.len - 1;
   return r;
 }

@@ -3,26 +3,33 @@
 // latent rows; the key is the full 576-wide latent+rope row and the value its leading 512
 // columns (weight absorption), so one gathered 1152-byte row serves all heads for both products.
 //
-// bf16 kernel: one workgroup = (query, KV split, group of 32 heads), 4 waves, 80 KB of LDS, so
-// two workgroups share a CU. The two head groups of one (query, split) sit next to each other
-// on one XCD and gather the same rows at about the same time: the second read comes from L2.
-//   * Tiles of 64 selected rows are gathered straight from HBM into one LDS stage with direct
-//     global->LDS 16-byte loads; the other workgroup on the CU computes while one waits. Each
-//     row's 72 chunks of 16 B are stored with the chunk slot XOR-ed by a 3-bit function of the
-//     row (swz) that keeps every MFMA operand read free of LDS bank conflicts.
+// bf16 kernel: one workgroup = (query, KV split, group of 64 heads), 8 waves, 160 KB of LDS, one
+// workgroup per CU. Waves 0-3 serve heads 0-31 of the group and waves 4-7 heads 32-63; both
+// halves compute on the same gathered tile.
+//   * Tiles of 64 selected rows are gathered straight from HBM into LDS with direct
+//     global->LDS 16-byte loads, double-buffered: the gathers of tile i+1 are in flight while
+//     tile i computes, and those of tile i+2 go out as soon as tile i's stage is consumed. The
+//     top of a tile waits until only the next tile's nine gathers per lane are outstanding, so
+//     the prefetch is never drained there. Each row's 72 chunks of 16 B are stored with the
+//     chunk slot XOR-ed by a 3-bit function of the row (swz) that keeps every MFMA operand read
+//     free of LDS bank conflicts.
+//   * The first indices and the query block are loaded before the sequence lookup, so the two
+//     latencies overlap at the start of the workgroup.
 //   * QK^T is computed transposed, S^T[rows x heads] = KV[rows x 576] * Q^T, on 32x32x16 MFMAs:
-//     wave (rb, kh) owns rows 32*rb.. and K half kh for all 32 heads; the query half is resident
-//     in registers (B operand). The two K-half partial sums of a row block are exchanged through
-//     LDS, each wave keeping half of the block's elements, so every lane holds one head.
+//     in each head half, wave (rb, kh) owns rows 32*rb.. and K half kh for all 32 heads; the
+//     query half is resident in registers (B operand). The two K-half partial sums of a row
+//     block are exchanged through LDS, each wave keeping half of the block's elements, so
+//     every lane holds one head.
 //   * Softmax in fp32 (base-2 exponent, scale*log2(e) folded into the logits) against a fixed
 //     reference maximum per head; P is rounded to bf16 into LDS.
-//   * P*V on 32x32x16 MFMAs: wave w owns value columns 128*w.. of all 32 heads; P is the A
-//     operand, V (row-major in the same LDS tile) is read column-wise with the gfx950
-//     transposing LDS read. The fp32 output block stays in registers across tiles.
+//   * P*V on 32x32x16 MFMAs: wave w of a head half owns value columns 128*w.. of its 32 heads;
+//     P is the A operand, V (row-major in the same LDS tile) is read column-wise with the
+//     gfx950 transposing LDS read. The fp32 output block stays in registers across tiles.
 //   * With several splits per query, each split stores its normalised partial output in bf16,
 //     in the accumulator register layout (32 contiguous bytes per lane and value block), and
 //     its log-sum-exp; a combine kernel merges them with exp(lse_i - lse) weights. With one
 //     split the output block is transposed through LDS and written with 16-byte stores.
+//   * Splits: about one workgroup per CU in total (256), down to one tile per split.
 #include <algorithm>
 
 #include "common.hpp"
@@ -33,22 +40,26 @@ namespace {
 
 constexpr int DQK = 576;
 constexpr int DV = 512;
-constexpr int HG = 32;                       // heads per workgroup
+constexpr int HG = 32;                       // heads of one head half (one per MFMA column)
+constexpr int WG_HEADS = 2 * HG;             // heads per workgroup
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = NWAVES * WAVE;      // 512
 constexpr int TILE = 64;                     // selected rows per LDS stage
 constexpr int ROWB = DQK * 2;                // 1152 bytes per latent row
 constexpr int CHUNKS = ROWB / 16;            // 72 chunks of 16 B
 constexpr int STAGE_BYTES = TILE * ROWB;     // 73728
 constexpr int ROPE_OFF = DV * 2;             // byte offset of the RoPE columns in a row
 constexpr int P_STRIDE = TILE + 8;           // bf16 elements per head row of P (padded)
-constexpr int OFF_R = STAGE_BYTES;           // 8 KB: QK half-sum exchange, then P
-constexpr int R_BYTES = 4 * 8 * 64 * 4;      // 8 floats per lane per wave
-constexpr int MLA_LDS = OFF_R + R_BYTES;     // 80 KB: two workgroups per CU
-constexpr int LOADS_PER_THREAD = STAGE_BYTES / 16 / 256;   // 18
+constexpr int R_BYTES = NWAVES * 8 * 64 * 4; // QK exchange (8 floats per lane per wave), then P
+constexpr int MLA_LDS = 2 * STAGE_BYTES + R_BYTES;   // 160 KB: one workgroup per CU
+constexpr int LOADS_PER_THREAD = STAGE_BYTES / 16 / NTHREADS;   // 9
 constexpr int QK_STEPS = DQK / 16 / 2;       // 18 MFMA k-steps per K half
 constexpr int VB_WAVE = DV / 32 / 4;         // 4 value blocks of 32 columns per wave
-static_assert(LOADS_PER_THREAD * 256 * 16 == STAGE_BYTES, "stage must split evenly");
-static_assert(HG * P_STRIDE * 2 <= R_BYTES, "P fits the exchange region");
-static_assert(2 * MLA_LDS <= 160 * 1024, "two workgroups per CU");
+static_assert(LOADS_PER_THREAD * NTHREADS * 16 == STAGE_BYTES, "stage must split evenly");
+static_assert(LOADS_PER_THREAD % 3 == 0, "gathers are issued in groups of three");
+static_assert(WG_HEADS * P_STRIDE * 2 <= R_BYTES, "P fits the exchange region");
+static_assert(WG_HEADS * DV * 2 <= STAGE_BYTES, "the output block fits one stage");
+static_assert(MLA_LDS <= 160 * 1024, "LDS of one CU");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,36 +75,63 @@ __device__ __forceinline__ int swz(int r) {
   return (2 * (r & 3) + ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (lane i writes lds_wave_base + 16*i), issued
+// as volatile inline assembly that the compiler does not see as a memory access: it then adds
+// no waits of its own for these loads (it would wait for all of them before any LDS access,
+// since it cannot tell the two stages apart), and the workgroup barriers do not drain them.
+// The kernel orders them itself: exact vmcnt waits before a stage is read, and a barrier
+// before a stage is refilled (volatile asm is never moved across the barrier's fence).
+__device__ __forceinline__ void gather16(const void* gptr, const char* lds_wave_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m));
+}
+
+// Lanes l and l^32 combined (max / sum), in every lane, with one gfx950 lane-half swap: of the
+// two results one holds the low half of x in both halves and the other the high half.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Hides a value from loop-invariant code motion so per-tile address math is recomputed
 // instead of occupying registers across the tile loop.
 __device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
 
 // Softmax statistics live in the RoPE columns of the tile being processed: those columns are
-// only read by QK^T, which every wave has finished before the first statistic is written.
-// Float i sits in row i/32 at RoPE byte 4*(i%32).
+// only read by QK^T, which every wave has finished before the first statistic is written, and
+// the prefetch writes the other stage. Float i sits in row i/32 at RoPE byte 4*(i%32).
 __device__ __forceinline__ float* stat(char* stage, int i) {
   return (float*)(stage + (i >> 5) * ROWB + ROPE_OFF + (i & 31) * 4);
 }
-constexpr int ST_MAX = 0;       // [4 waves][HG] maximum over each wave's 16 rows
-constexpr int ST_SUM = 128;     // [4 waves][HG] sums over the same rows
-constexpr int ST_FLAG = 256;    // [4]           wave saw a logit beyond its reference headroom
+constexpr int ST_MAX = 0;       // [8 waves][HG] maximum over each wave's 16 rows
+constexpr int ST_SUM = 256;     // [8 waves][HG] sums over the same rows
+constexpr int ST_FLAG = 512;    // [8]           wave saw a logit beyond its reference headroom
+constexpr int ST_FAC = 576;     // [2][HG]       rescale factors of raised references
 
 // Element r of the QK accumulator kept by K-half wave kh after the exchange: value q (0..7) of
 // the wave is element 8*(q/4) + 4*kh + q%4; the other eight go to the partner wave.
 __device__ __forceinline__ int kept_elem(int q, int kh) { return 8 * (q >> 2) + 4 * kh + (q & 3); }
 
-// grid: 1-D, 8 * ceil(T/8) * nsplit * (H/32) workgroups. Consecutive workgroups are dispatched
-// round-robin to the 8 XCDs; the mapping gives every workgroup of one query the same XCD, and
-// puts the two head halves of one (query, split) next to each other there, so the second read
-// of each gathered row is served by that XCD's L2.
-__global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
+// grid: 1-D, 8 * ceil(T/8) * nsplit * ceil(H/64) workgroups. Consecutive workgroups are
+// dispatched round-robin to the 8 XCDs; the mapping gives every workgroup of one query the same
+// XCD, so the query block and the split partials of a query stay in one L2.
+__global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ indices, int k, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int H,
-    float scale_log2, int nsplit, int rows_per_split, int tgroups, __bf16* __restrict__ out,
+    float scale_log2, int nsplit, int rows_per_split, __bf16* __restrict__ out,
     float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int nhg = H / HG;
+  // Separate LDS objects let the compiler see that the gathers streaming into one stage never
+  // alias reads of the other stage or of the exchange region, so it adds no waits of its own.
+  __shared__ __attribute__((aligned(16))) char stage0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char rbuf[R_BYTES];
+  const int nhg = (H + WG_HEADS - 1) / WG_HEADS;
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
   const int hg = kk % nhg;
@@ -106,80 +144,155 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c32 = lane & 31;
-  const int kh = wave & 1;        // QK: K half (columns 288*kh ..); softmax: kept element set
-  const int rb = wave >> 1;       // QK: row block (rows 32*rb ..)
-  const int cq = wave;            // PV: value columns 128*cq ..
+  const int hl = wave >> 2;       // head half of the workgroup
+  const int w4 = wave & 3;        // wave within the head half
+  const int kh = w4 & 1;          // QK: K half (columns 288*kh ..); softmax: kept element set
+  const int rb = w4 >> 1;         // QK: row block (rows 32*rb ..)
+  const int cq = w4;              // PV: value columns 128*cq ..
+  const int g32 = 2 * hg + hl;    // 32-head group of this head half
+  // With H an odd multiple of 32 the upper half of the last group has no heads: it computes on
+  // the first group's queries (keeping every wave in step) and writes nothing.
+  const bool heads_valid = g32 * HG < H;
 
-  const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, t);
-  const int64_t L = qp.len;
-  const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
   const int r_beg = split * rows_per_split;
   const int r_end = min(k, r_beg + rows_per_split);
-  const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const int32_t* irow = indices + (int64_t)t * k;
+  // The first two tiles' indices do not depend on the sequence lookup, so their loads go out
+  // before it and the latencies overlap. (Loaded even if the split turns out to be empty: every
+  // address is inside its array.) The query block is loaded behind the first gathers.
+  bf16x8 qreg[QK_STEPS];
+  int i_even = irow[min(r_beg + lane, k - 1)];          // indices of the next even / odd tile
+  int i_odd = irow[min(r_beg + TILE + lane, k - 1)];
+  // The sequence lookup is done by one wave and shared through LDS: every workgroup of the grid
+  // starts at once and reads the same few cache lines of cu_seqlens.
+  QueryPos qp;
+  {
+    int64_t* qs = (int64_t*)rbuf;
+    if (wave == 0) {
+      const QueryPos q0 = query_pos(cu_q, cu_k, nseq, total_k, t);
+      if (lane == 0) {
+        qs[0] = q0.p;
+        qs[1] = q0.key_base;
+        qs[2] = q0.len;
+      }
+    }
+    __syncthreads();
+    qp.p = qs[0];
+    qp.key_base = qs[1];
+    qp.len = qs[2];
+    qp.b = 0;
+  }
+  const int64_t L = qp.len;
+  const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
+  const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const __bf16* kvb = kv + qp.key_base * DQK;
-  char* stage = lds;
-  float* xch = (float*)(lds + OFF_R);         // [4 waves][8][64]
-  __bf16* pl = (__bf16*)(lds + OFF_R);        // [HG][P_STRIDE], after the exchange is read
+  float* xch = (float*)rbuf;                  // [8 waves][8][64]
+  __bf16* pl = (__bf16*)rbuf;                 // [64 heads][P_STRIDE], after the exchange is read
 
   // Softmax with a fixed reference maximum per head: the first tile in which a head has a finite
   // logit sets its reference m_ref, and probabilities are exp2(s - m_ref) without rescaling the
-  // output block. If a later tile exceeds a reference by more than 2^kHeadroom, the workgroup
-  // raises the references and restarts its split (softmax is shift-invariant, so the result is
-  // the same). Every update of the output accumulators stays in the MFMA pipe.
+  // output block. Only if a later tile exceeds a reference by more than 2^kHeadroom is it raised,
+  // with the head's output block and running sum scaled by exp2(old - new) (online softmax).
   f32x16 o[VB_WAVE];
-  float m_ref = -INFINITY, l_run = 0.f;
-  auto zero_o = [&]() {                       // 0 x 0 + 0 on the matrix core keeps o in AGPRs
+  float l_run = 0.f;
+  // reference maxima of head c32 in both head halves: every wave tracks both and updates them
+  // from the same shared statistics, so every decision on them is uniform across the workgroup
+  float mref0 = -INFINITY, mref1 = -INFINITY;
+  {                                           // 0 x 0 + 0 on the matrix core keeps o in AGPRs
     const bf16x8 z = {};
 #pragma unroll
     for (int db = 0; db < VB_WAVE; ++db) o[db] = mfma32x32x16(z, z, f32x16{});
-  };
-  zero_o();
+  }
 
   if (ntiles > 0) {
-    // index of tile row `lane`, -1 past the split
-    auto load_idx = [&](int tile) -> int {
-      const int r = r_beg + tile * TILE + lane;
-      const int v = irow[min(r, k - 1)];
-      return (tile < ntiles && r < r_end) ? v : -1;
+    // Index of tile row `lane` as loaded: the load is issued for every tile number, clamped into
+    // the row, so that each tile costs the same number of memory operations. Rows past the split
+    // are masked where the index is used (a select right after the load would wait for it).
+    auto load_idx = [&](int tile) __attribute__((always_inline)) -> int {
+      return irow[min(r_beg + tile * TILE + lane, k - 1)];
     };
-    // gathers one tile: slot c*256+tid of the stage holds chunk (slot%72)^swz(row) of row
+    auto masked = [&](int tile, int v) __attribute__((always_inline)) -> int {
+      return (tile < ntiles && r_beg + tile * TILE + lane < r_end) ? v : -1;
+    };
+    // gathers one tile into stage `stg`: slot c*512+tid holds chunk (slot%72)^swz(row) of row
     // slot/72 (invalid rows read row 0 and are masked later)
-    auto issue = [&](int idxv) {
+    auto issue = [&](char* stg, int tile, int idx_raw) __attribute__((always_inline)) {
+      const int idxv = masked(tile, idx_raw);
       int tt = tid;
       opaque(tt);
 #pragma unroll
-      for (int g = 0; g < LOADS_PER_THREAD / 6; ++g) {
-        int vs[6], gcs[6];
+      for (int g = 0; g < LOADS_PER_THREAD / 3; ++g) {
+        int vs[3], gcs[3];
 #pragma unroll
-        for (int j = 0; j < 6; ++j) {
-          const int slot = (g * 6 + j) * 256 + tt;
+        for (int j = 0; j < 3; ++j) {
+          // the 64 slots of this wave lie in rows r0 and r0+1 (72 slots per row): two scalar
+          // reads of the index register instead of a cross-lane shuffle
+          const int sbase = (g * 3 + j) * NTHREADS + wave * 64;      // wave-uniform
+          const int r0 = sbase / CHUNKS;
+          const int slot = (g * 3 + j) * NTHREADS + tt;
           const int row = slot / CHUNKS;
           gcs[j] = (slot - row * CHUNKS) ^ swz(row);
-          vs[j] = __shfl(idxv, row, WAVE);
+          const int i0 = __builtin_amdgcn_readlane(idxv, r0);
+          const int i1 = __builtin_amdgcn_readlane(idxv, min(r0 + 1, TILE - 1));
+          vs[j] = row == r0 ? i0 : i1;
         }
 #pragma unroll
-        for (int j = 0; j < 6; ++j) {
+        for (int j = 0; j < 3; ++j) {
           const uint32_t v = (uint32_t)vs[j] < Lu ? (uint32_t)vs[j] : 0u;
-          global_to_lds16(kvb + (size_t)v * DQK + gcs[j] * 8,
-                          stage + ((g * 6 + j) * 256 + wave * 64) * 16);
+          gather16(kvb + (size_t)v * DQK + gcs[j] * 8, stg + ((g * 3 + j) * NTHREADS + wave * 64) * 16);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the groups apart: bounded live registers
       }
     };
-
-    // the first tile's gathers go out as soon as its indices arrive; the query block loads
-    // behind them and both are waited for at the top of the first tile
-    int idx_cur = load_idx(0);
-    wait_all_memory();
-    issue(idx_cur);
-    bf16x8 qreg[QK_STEPS];
+    // Double buffering: tile j computes in stage j%2 while the gathers of tile j+1 stream into
+    // the other stage. The indices of tile j+2 are loaded at the top of tile j (into the
+    // register that held tile j's). At the end of tile j each wave waits for all its memory
+    // operations (the gathers of tile j+1 have had a whole tile of compute to land), and one
+    // barrier then both frees stage j and publishes tile j+1; the gathers of tile j+2 follow.
+    // row-validity masks of the next even / odd tile, taken right after a full wait (so the
+    // compiler never has to wait for an index load at the top of a tile)
+    uint64_t vm_even = 0, vm_odd = 0;
     {
-      const __bf16* qr = q + ((int64_t)t * H + hg * HG + c32) * DQK + kh * (QK_STEPS * 16) +
-                         half * 8;
+      wait_all_memory();
+      vm_even = __ballot((uint32_t)masked(0, i_even) < Lu);
+      vm_odd = __ballot((uint32_t)masked(1, i_odd) < Lu);
+      issue(stage0, 0, i_even);
+      // The query block [64 heads x 576] has the shape of a tile: it is gathered the same way,
+      // coalesced, into stage 1 (the upper half of the last group of an odd number of 32-head
+      // groups reads heads 0..31 again), and each wave reads its B operands from there with
+      // the same conflict-free pattern as the QK A operands.
+      {
+        int tt = tid;
+        opaque(tt);
+        const __bf16* qt = q + (int64_t)t * H * DQK;
 #pragma unroll
-      for (int i = 0; i < QK_STEPS; ++i) qreg[i] = *(const bf16x8*)(qr + i * 16);
+        for (int j = 0; j < LOADS_PER_THREAD; ++j) {
+          const int slot = j * NTHREADS + tt;
+          const int row = slot / CHUNKS;
+          const int head = hg * WG_HEADS + row < H ? hg * WG_HEADS + row : (row & (HG - 1));
+          gather16(qt + (int64_t)head * DQK + ((slot - row * CHUNKS) ^ swz(row)) * 8,
+                   stage1 + (j * NTHREADS + wave * 64) * 16);
+        }
+      }
+      wait_all_memory();                       // tile 0 and the query block
+      __syncthreads();
+      {
+        const int row = hl * HG + c32;
+        const int sq = swz(row);
+#pragma unroll
+        for (int i = 0; i < QK_STEPS; ++i) {
+          const int chunk = 36 * kh + 2 * i + half;
+          qreg[i] = *(const bf16x8*)(stage1 + row * ROWB + ((chunk ^ sq) << 4));
+        }
+        // in registers before stage 1 is refilled (and before any use in the loop)
+#pragma unroll
+        for (int i = 0; i < QK_STEPS; ++i) asm volatile("" : "+v"(qreg[i]));
+      }
+      __syncthreads();
+      // tile 1 streams in while tile 0 computes
+      if (1 < ntiles) issue(stage1, 1, i_odd);
     }
+
     // A-operand lane bases: step i reads chunk 36*kh + 2*i + half of row 32*rb + c32; with
     // u = 2*kh + i the slot is 8*(4*kh + u/4) + ((2*(u%4) + half) ^ swz): four lane bases plus
     // 128*(i/4) immediates.
@@ -192,46 +305,44 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
                  (((2 * (u & 3) + half) ^ sw) << 4);
     }
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int idx_nxt = load_idx(tile + 1);
-      wait_all_memory();                       // this tile's gathers (and the index load)
-      __syncthreads();
-      const uint64_t vmask = __ballot((uint32_t)idx_cur < Lu);
-
-      // ---- QK^T half sums: S^T[32 rows x 32 heads] over this wave's 288 columns
-      f32x16 s = {};
-      {
-        bf16x8 a[2];
-        auto rd = [&](int i, int b) { a[b] = *(const bf16x8*)(stage + abase[i & 3] + (i >> 2) * 128); };
-        rd(0, 0);
-#pragma unroll
-        for (int i = 0; i < QK_STEPS; ++i) {
-          if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
-          s = mfma32x32x16(a[i & 1], qreg[i], s);
-        }
-      }
-      // ---- exchange half sums: keep element set kh, hand the other to the partner wave
-#pragma unroll
-      for (int qi = 0; qi < 8; ++qi) xch[(wave * 8 + qi) * 64 + lane] = s[kept_elem(qi, kh ^ 1)];
-      __syncthreads();
-      float sv[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int qi = 0; qi < 8; ++qi) {
-        const int e = kept_elem(qi, kh);
-        const float v = s[e] + xch[((wave ^ 1) * 8 + qi) * 64 + lane];
-        const int row = 32 * rb + mfma32_row(e, lane);
-        sv[qi] = ((vmask >> row) & 1) ? v * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[qi]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const int w0 = 4 * hl;                     // first wave of this head half
+    auto tile_max = [&](char* stage, int h) __attribute__((always_inline)) -> float {
+      return fmaxf(fmaxf(*stat(stage, ST_MAX + (4 * h + 0) * HG + c32), *stat(stage, ST_MAX + (4 * h + 1) * HG + c32)),
+                   fmaxf(*stat(stage, ST_MAX + (4 * h + 2) * HG + c32), *stat(stage, ST_MAX + (4 * h + 3) * HG + c32)));
+    };
+    // Tile maxima through LDS (every wave's row maxima, one barrier): unset references are set;
+    // a reference exceeded by more than the headroom is raised to the tile maximum, and the
+    // output block and running sum of its head are scaled by exp2(old - new) (online softmax;
+    // rare, so the common path keeps every accumulator update on the matrix core).
+    auto update_refs = [&](char* stage, float mx) __attribute__((always_inline)) {
       if (half == 0) *stat(stage, ST_MAX + wave * HG + c32) = mx;
-      __syncthreads();                         // the exchange region is free for P from here
-      const float m_tile =
-          fmaxf(fmaxf(*stat(stage, ST_MAX + 0 * HG + c32), *stat(stage, ST_MAX + 1 * HG + c32)),
-                fmaxf(*stat(stage, ST_MAX + 2 * HG + c32), *stat(stage, ST_MAX + 3 * HG + c32)));
-      const bool exceed = m_ref != -INFINITY && m_tile > m_ref + kHeadroom;
-      if (m_ref == -INFINITY || exceed) m_ref = m_tile;
+      __syncthreads();
+      const float mt0 = tile_max(stage, 0), mt1 = tile_max(stage, 1);
+      const bool r0 = mref0 != -INFINITY && mt0 > mref0 + kHeadroom;
+      const bool r1 = mref1 != -INFINITY && mt1 > mref1 + kHeadroom;
+      const float f0 = r0 ? __builtin_amdgcn_exp2f(mref0 - mt0) : 1.f;
+      const float f1 = r1 ? __builtin_amdgcn_exp2f(mref1 - mt1) : 1.f;
+      if (mref0 == -INFINITY || r0) mref0 = mt0;
+      if (mref1 == -INFINITY || r1) mref1 = mt1;
+      if (__ballot(r0 || r1) != 0) {           // uniform across the workgroup
+        if (wave == 0 && half == 0) {
+          *stat(stage, ST_FAC + c32) = f0;
+          *stat(stage, ST_FAC + HG + c32) = f1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float f = *stat(stage, ST_FAC + hl * HG + mfma32_row(r, lane));
+#pragma unroll
+          for (int db = 0; db < VB_WAVE; ++db) o[db][r] *= f;
+        }
+        l_run *= hl ? f1 : f0;
+      }
+    };
+    // probabilities exp2(s - m_ref) of this wave's 16 rows for head c32 into P (bf16) and
+    // their sum into the statistics
+    auto write_p = [&](char* stage, const float (&sv)[8]) __attribute__((always_inline)) {
+      const float m_ref = hl ? mref1 : mref0;
       const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       float ls = 0.f;
 #pragma unroll
@@ -245,28 +356,82 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
           pk[e] = (__bf16)p;
         }
         const int row0 = 32 * rb + 16 * g + 8 * kh + 4 * half;
-        *(bf16x4*)(pl + c32 * P_STRIDE + row0) = pk;
+        *(bf16x4*)(pl + (hl * HG + c32) * P_STRIDE + row0) = pk;
       }
-      ls += __shfl_xor(ls, 32, WAVE);
+      ls = halves_sum(ls);
       if (half == 0) *stat(stage, ST_SUM + wave * HG + c32) = ls;
+    };
+
+    // One tile in stage `stage`; idx holds the indices of this tile and receives those of
+    // tile+2, vm the row-validity mask of this tile and then of tile+2.
+    auto step = [&](char* stage, int tile, int& idx, uint64_t& vm) __attribute__((always_inline)) {
+      const uint64_t vmask = vm;
+      idx = load_idx(tile + 2);
+
+      // ---- QK^T half sums: S^T[32 rows x 32 heads] over this wave's 288 columns
+      f32x16 s = {};
+      {
+        bf16x8 a[2];
+        auto rd = [&](int i, int b) __attribute__((always_inline)) { a[b] = *(const bf16x8*)(stage + abase[i & 3] + (i >> 2) * 128); };
+        rd(0, 0);
+#pragma unroll
+        for (int i = 0; i < QK_STEPS; ++i) {
+          if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
+          s = mfma32x32x16(a[i & 1], qreg[i], s);
+        }
+      }
+      // ---- exchange half sums: keep element set kh, hand the other to the partner wave
+      // kh is wave-uniform; both candidate elements are read at compile-time positions and made
+      // opaque (an empty asm, no instruction) so the selects are not folded back into an indexed
+      // register move
+      float e0[8], e1[8];
+#pragma unroll
+      for (int qi = 0; qi < 8; ++qi) {
+        e0[qi] = s[kept_elem(qi, 0)];
+        e1[qi] = s[kept_elem(qi, 1)];
+        asm volatile("" : "+v"(e0[qi]), "+v"(e1[qi]));
+        xch[(wave * 8 + qi) * 64 + lane] = kh ? e0[qi] : e1[qi];
+      }
+      __syncthreads();
+      // the partner's eight values are all read before any is used (otherwise each read sinks
+      // into the branch of its row-validity test and the reads serialise)
+      float part[8];
+#pragma unroll
+      for (int qi = 0; qi < 8; ++qi) part[qi] = xch[((wave ^ 1) * 8 + qi) * 64 + lane];
+#pragma unroll
+      for (int qi = 0; qi < 8; ++qi) asm volatile("" : "+v"(part[qi]));
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int qi = 0; qi < 8; ++qi) {
+        const float mine = kh ? e1[qi] : e0[qi];
+        const float v = (mine + part[qi]) * scale_log2;
+        const int row = 32 * rb + mfma32_row(kept_elem(qi, kh), lane);
+        sv[qi] = ((vmask >> row) & 1) ? v : -INFINITY;
+        mx = fmaxf(mx, sv[qi]);
+      }
+      mx = halves_max(mx);                     // this wave's 16 rows, head c32 of its half
+      // The tile maxima are exchanged only while some reference is unset; afterwards a logit
+      // beyond its reference's headroom is detected from the wave's own rows and flagged with
+      // the probabilities.
+      const bool need_max = __ballot(mref0 == -INFINITY || mref1 == -INFINITY) != 0;
+      if (need_max) update_refs(stage, mx);
+      write_p(stage, sv);
+      const float m_ref = hl ? mref1 : mref0;
+      const bool exceed = !need_max && mx > m_ref + kHeadroom;
       const bool wave_exceeds = __ballot(exceed) != 0;   // ballot with every lane active
       if (lane == 0) *stat(stage, ST_FLAG + wave) = wave_exceeds ? 1.f : 0.f;
       __syncthreads();
-      const bool restart = (*stat(stage, ST_FLAG + 0) + *stat(stage, ST_FLAG + 1) +
-                            *stat(stage, ST_FLAG + 2) + *stat(stage, ST_FLAG + 3)) != 0.f;
-      if (restart) {                           // uniform across the workgroup: redo the split
-        wait_all_memory();
+      float flags = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVES; ++w) flags += *stat(stage, ST_FLAG + w);
+      if (flags != 0.f) {                      // uniform: raise, rescale, redo the probabilities
+        update_refs(stage, mx);
+        write_p(stage, sv);
         __syncthreads();
-        zero_o();
-        l_run = 0.f;
-        idx_cur = load_idx(0);
-        wait_all_memory();
-        issue(idx_cur);
-        tile = -1;
-        continue;
       }
-      l_run += (*stat(stage, ST_SUM + 0 * HG + c32) + *stat(stage, ST_SUM + 1 * HG + c32)) +
-               (*stat(stage, ST_SUM + 2 * HG + c32) + *stat(stage, ST_SUM + 3 * HG + c32));
+      l_run += (*stat(stage, ST_SUM + (w0 + 0) * HG + c32) + *stat(stage, ST_SUM + (w0 + 1) * HG + c32)) +
+               (*stat(stage, ST_SUM + (w0 + 2) * HG + c32) + *stat(stage, ST_SUM + (w0 + 3) * HG + c32));
 
       // ---- O[32 heads x 128 cols] += P[32 heads x 64 rows] * V[64 rows x 128 cols]
       // V[krow][col] for the B operand of value block blk (32 columns), rows 4*rr.. of the
@@ -289,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
           vb[rr][0] = pp + 64 * b2;    // even blk: blk ^ b2 = blk + b2
           vb[rr][1] = pp - 64 * b2;    // odd blk:  blk ^ b2 = blk - b2
         }
-        const __bf16* pbase = pl + c32 * P_STRIDE + half * 8;
+        const __bf16* pbase = pl + (hl * HG + c32) * P_STRIDE + half * 8;
 #pragma unroll
         for (int ks = 0; ks < TILE / 16; ++ks) {
           const bf16x8 pa = *(const bf16x8*)(pbase + ks * 16);
@@ -302,65 +467,77 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
           }
         }
       }
-      // the stage and P are free once every wave is past this point: next tile's gathers
+      // end of the tile: this wave's memory operations (the next tile's gathers and the index
+      // load) complete, then one barrier frees this stage and P and publishes the next tile.
+      // (Unconditional, also after the last tile: the compiler then knows every index load is
+      // complete before the next tile and adds no wait of its own, which would also drain the
+      // gathers it cannot see.)
+      wait_all_memory();
+      vm = __ballot((uint32_t)masked(tile + 2, idx) < Lu);
       __syncthreads();
-      if (tile + 1 < ntiles) issue(idx_nxt);
-      idx_cur = idx_nxt;
+      if (tile + 2 < ntiles) issue(stage, tile + 2, idx);
+    };
+    for (int tile = 0; tile < ntiles; tile += 2) {   // unrolled by two: each step names its stage
+      step(stage0, tile, i_even, vm_even);
+      if (tile + 1 < ntiles) step(stage1, tile + 1, i_odd, vm_odd);
     }
+    wait_all_memory();
   }
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
-  float* fin = (float*)(lds + OFF_R);          // [0,32): l per head, [32,64): max per head
+  float* fin = (float*)rbuf;                   // [0,64): l per head, [64,128): max per head
   __syncthreads();
-  if (wave == 0 && half == 0) {
-    fin[c32] = l_run;
-    fin[HG + c32] = m_ref;
+  if (w4 == 0 && half == 0) {
+    fin[hl * HG + c32] = l_run;
+    fin[WG_HEADS + hl * HG + c32] = hl ? mref1 : mref0;
   }
   __syncthreads();
   float inv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float l = fin[mfma32_row(r, lane)];
+    const float l = fin[hl * HG + mfma32_row(r, lane)];
     inv[r] = l > 0.f ? 1.f / l : 0.f;
   }
+  const int nhg32 = H / HG;
   if (nsplit > 1) {
     // partial output in the accumulator layout: per (wave, value block) each lane stores its
     // 16 values as 32 contiguous bytes, so a wave writes 2 KB contiguous per block
-    __bf16* po = part_o + ((((int64_t)t * nsplit + split) * nhg + hg) * 4 + wave) *
-                              (VB_WAVE * 1024);
+    if (heads_valid) {
+      __bf16* po = part_o + ((((int64_t)t * nsplit + split) * nhg32 + g32) * 4 + w4) *
+                                (VB_WAVE * 1024);
 #pragma unroll
-    for (int db = 0; db < VB_WAVE; ++db) {
-      bf16x8 lo8, hi8;
+      for (int db = 0; db < VB_WAVE; ++db) {
+        bf16x8 lo8, hi8;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        lo8[r] = (__bf16)(o[db][r] * inv[r]);
-        hi8[r] = (__bf16)(o[db][8 + r] * inv[8 + r]);
+        for (int r = 0; r < 8; ++r) {
+          lo8[r] = (__bf16)(o[db][r] * inv[r]);
+          hi8[r] = (__bf16)(o[db][8 + r] * inv[8 + r]);
+        }
+        *(bf16x8*)(po + (db * 64 + lane) * 16) = lo8;
+        *(bf16x8*)(po + (db * 64 + lane) * 16 + 8) = hi8;
       }
-      *(bf16x8*)(po + (db * 64 + lane) * 16) = lo8;
-      *(bf16x8*)(po + (db * 64 + lane) * 16 + 8) = hi8;
     }
   } else {
-    // final output: transpose the [32 heads x 512] block through LDS, then 16-byte stores
-    __bf16* ot = (__bf16*)lds;
+    // final output: transpose the [64 heads x 512] block through LDS, then 16-byte stores
+    __bf16* ot = (__bf16*)stage0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int hl = mfma32_row(r, lane);
+      const int hr = hl * HG + mfma32_row(r, lane);
 #pragma unroll
       for (int db = 0; db < VB_WAVE; ++db)
-        ot[hl * DV + (VB_WAVE * cq + db) * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
+        ot[hr * DV + (VB_WAVE * cq + db) * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
     }
     __syncthreads();
-    __bf16* ob = out + ((int64_t)t * H + hg * HG) * DV;
-#pragma unroll 4
-    for (int i = 0; i < HG * DV / 8 / 256; ++i) {
-      const int piece = i * 256 + tid;
+    __bf16* ob = out + ((int64_t)t * H + hg * WG_HEADS) * DV;
+    const int heads = min(WG_HEADS, H - hg * WG_HEADS);
+    const int pieces = heads * DV / 8;
+    for (int piece = tid; piece < pieces; piece += NTHREADS)
       *(bf16x8*)(ob + piece * 8) = *(const bf16x8*)(ot + piece * 8);
-    }
   }
-  if (wave == 0 && half == 0) {
-    const float l = fin[c32];
-    const float val = l > 0.f ? (fin[HG + c32] + log2f(l)) * kLn2 : -INFINITY;
-    const int64_t h = hg * HG + c32;
+  if (w4 == 0 && half == 0 && heads_valid) {
+    const float l = fin[hl * HG + c32];
+    const float val = l > 0.f ? (fin[WG_HEADS + hl * HG + c32] + log2f(l)) * kLn2 : -INFINITY;
+    const int64_t h = g32 * HG + c32;
     if (nsplit == 1) {
       if (lse) lse[(int64_t)t * H + h] = val;
     } else {
@@ -369,69 +546,96 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_bf16(
   }
 }
 
-// Merges the splits of one (query, 32-head group, wave, value block): 64 lanes, each with the
-// 16 (head, column) values the sparse kernel's accumulator layout gives it.
-// out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i (natural-log units).
-__global__ __launch_bounds__(64) void mla_combine(const __bf16* __restrict__ part_o,
-                                                  const float* __restrict__ part_lse,
-                                                  int nsplit, int H, __bf16* __restrict__ out,
-                                                  float* __restrict__ lse) {
+// Merges the splits of one (query, 32-head group, wave, value block): the block's 1024 outputs
+// are the 16 (head, column) values that each of 64 lanes holds in the sparse kernel's
+// accumulator layout. out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i
+// (natural-log units). Four waves share the splits (wave q takes splits q, q+4, ..); each lane
+// issues all loads of a pass before the weights are known, and the four partial sums meet in
+// LDS.
+constexpr int CMB_THREADS = 256;
+constexpr int CMB_SPW = 8;                     // splits per wave and pass
+
+__global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           int nsplit, int H,
+                                                           __bf16* __restrict__ out,
+                                                           float* __restrict__ lse) {
   extern __shared__ float wgt[];               // [nsplit][32] merge weights per head
+  __shared__ float red[3][16][WAVE];           // partial sums of waves 1..3
   const int t = blockIdx.x;
   const int y = blockIdx.y;
   const int db = y % VB_WAVE;
   const int w = (y / VB_WAVE) % 4;
-  const int hg = y / (VB_WAVE * 4);
-  const int nhg = H / HG;
-  const int lane = threadIdx.x;
-  const int h0 = hg * HG;                      // first head of this group
-  // every split's log-sum-exp of the group's 32 heads, one coalesced load per lane and pass
-  for (int j = lane; j < nsplit * 32; j += 64)
+  const int g32 = y / (VB_WAVE * 4);
+  const int nhg32 = H / HG;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid >> 6;
+  const int h0 = g32 * HG;                     // first head of this group
+  const int64_t stride = (int64_t)nhg32 * 4 * VB_WAVE * 1024;     // elements per (t, split)
+  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((g32 * 4 + w) * VB_WAVE + db) * 1024 +
+                     lane * 16;
+  bf16x8 lo8[CMB_SPW], hi8[CMB_SPW];
+  auto load = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < CMB_SPW; ++j) {
+      const int i = base + wv + 4 * j;
+      if (i < nsplit) {
+        lo8[j] = *(const bf16x8*)(po + i * stride);
+        hi8[j] = *(const bf16x8*)(po + i * stride + 8);
+      }
+    }
+  };
+  load(0);
+  // every split's log-sum-exp of the group's 32 heads
+  for (int j = tid; j < nsplit * 32; j += CMB_THREADS)
     wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
   __syncthreads();
-  if (lane < 32) {
+  if (tid < 32) {
     float mx = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, wgt[i * 32 + lane]);
+    for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, wgt[i * 32 + tid]);
     float sum = 0.f;
     if (mx != -INFINITY)
-      for (int i = 0; i < nsplit; ++i) sum += expf(wgt[i * 32 + lane] - mx);
+      for (int i = 0; i < nsplit; ++i) sum += expf(wgt[i * 32 + tid] - mx);
     const float tot = (mx == -INFINITY) ? -INFINITY : mx + logf(sum);
     for (int i = 0; i < nsplit; ++i) {
-      const float li = wgt[i * 32 + lane];
-      wgt[i * 32 + lane] = (li == -INFINITY) ? 0.f : expf(li - tot);
+      const float li = wgt[i * 32 + tid];
+      wgt[i * 32 + tid] = (li == -INFINITY) ? 0.f : expf(li - tot);
     }
-    if (lse && w == 0 && db == 0) lse[(int64_t)t * H + h0 + lane] = tot;
+    if (lse && w == 0 && db == 0) lse[(int64_t)t * H + h0 + tid] = tot;
   }
   __syncthreads();
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int64_t stride = (int64_t)nhg * 4 * VB_WAVE * 1024;     // elements per (t, split)
-  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((hg * 4 + w) * VB_WAVE + db) * 1024 +
-                     lane * 16;
-  auto add = [&](int i, bf16x8 lo8, bf16x8 hi8) {
+  for (int base = 0;;) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      acc[r] += wgt[i * 32 + mfma32_row(r, lane)] * (float)lo8[r];
-      acc[8 + r] += wgt[i * 32 + mfma32_row(8 + r, lane)] * (float)hi8[r];
+    for (int j = 0; j < CMB_SPW; ++j) {
+      const int i = base + wv + 4 * j;
+      if (i < nsplit) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          acc[r] += wgt[i * 32 + mfma32_row(r, lane)] * (float)lo8[j][r];
+          acc[8 + r] += wgt[i * 32 + mfma32_row(8 + r, lane)] * (float)hi8[j][r];
+        }
+      }
     }
-  };
-  int i = 0;
-  for (; i + 4 <= nsplit; i += 4) {            // four splits' loads in flight at once
-    bf16x8 lo8[4], hi8[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo8[j] = *(const bf16x8*)(po + (i + j) * stride);
-      hi8[j] = *(const bf16x8*)(po + (i + j) * stride + 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) add(i + j, lo8[j], hi8[j]);
+    base += 4 * CMB_SPW;
+    if (base >= nsplit) break;
+    load(base);
   }
-  for (; i < nsplit; ++i)
-    add(i, *(const bf16x8*)(po + i * stride), *(const bf16x8*)(po + i * stride + 8));
-  __bf16* ob = out + ((int64_t)t * H + h0) * DV + (VB_WAVE * w + db) * 32 + (lane & 31);
+  if (wv > 0) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ob[(int64_t)mfma32_row(r, lane) * DV] = (__bf16)acc[r];
+    for (int r = 0; r < 16; ++r) red[wv - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wv == 0) {
+    __bf16* ob = out + ((int64_t)t * H + h0) * DV + (VB_WAVE * w + db) * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      ob[(int64_t)mfma32_row(r, lane) * DV] =
+          (__bf16)(acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane]);
+  }
 }
 
 // fp32 path: one workgroup per (query, head); logits of the selected rows live in LDS.
@@ -500,10 +704,10 @@ __global__ __launch_bounds__(256) void sparse_mla_f32(
 MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
   MlaPlan p;
   const int tiles = (k + TILE - 1) / TILE;
-  const int64_t wgs = (int64_t)b.total_q * (n_heads / HG);
+  const int64_t wgs = (int64_t)b.total_q * ((n_heads + WG_HEADS - 1) / WG_HEADS);
   const int64_t wgs1 = wgs > 0 ? wgs : 1;
-  int nsplit = (int)((512 + wgs1 - 1) / wgs1);          // two workgroups per CU
-  nsplit = std::max(1, std::min(nsplit, (tiles + 1) / 2));          // at least 2 tiles per split
+  int nsplit = (int)((256 + wgs1 - 1) / wgs1);          // one workgroup per CU
+  nsplit = std::max(1, std::min(nsplit, tiles));
   const int tiles_per_split = (tiles + nsplit - 1) / nsplit;
   p.rows_per_split = tiles_per_split * TILE;
   p.nsplit = (k + p.rows_per_split - 1) / p.rows_per_split;
@@ -517,9 +721,6 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
                                   const int32_t* indices, int k, int n_heads, float scale,
                                   void* out, float* lse, void* workspace, const MlaPlan& plan,
                                   hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_bf16,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, MLA_LDS);
-  if (e != hipSuccess) return e;
   float* part_lse = nullptr;
   __bf16* part_o = nullptr;
   if (plan.nsplit > 1) {
@@ -527,15 +728,17 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
     part_o = (__bf16*)(part_lse + (size_t)b.total_q * plan.nsplit * n_heads);
   }
   const int tgroups = (b.total_q + 7) / 8;
-  const int64_t nblocks = (int64_t)8 * tgroups * plan.nsplit * (n_heads / HG);
-  sparse_mla_bf16<<<dim3((unsigned)nblocks), 256, MLA_LDS, stream>>>(
+  const int64_t nblocks =
+      (int64_t)8 * tgroups * plan.nsplit * ((n_heads + WG_HEADS - 1) / WG_HEADS);
+  sparse_mla_bf16<<<dim3((unsigned)nblocks), NTHREADS, 0, stream>>>(
       (const __bf16*)q, (const __bf16*)kv, indices, k, b.cu_q, b.cu_k, b.nseq, b.total_q,
-      b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, tgroups,
-      (__bf16*)out, lse, part_o, part_lse);
-  e = hipGetLastError();
+      b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, (__bf16*)out, lse,
+      part_o, part_lse);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 4 * VB_WAVE), 64, plan.nsplit * 32 * sizeof(float),
-                stream>>>(part_o, part_lse, plan.nsplit, n_heads, (__bf16*)out, lse);
+  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 4 * VB_WAVE), CMB_THREADS,
+                plan.nsplit * 32 * sizeof(float), stream>>>(part_o, part_lse, plan.nsplit, n_heads,
+                                                            (__bf16*)out, lse);
   return hipGetLastError();
 }
 
