@@ -13,10 +13,12 @@
 //    it, so the workgroup reads one contiguous stream. Key rows go straight from HBM into
 //    registers (B operand), two steps ahead, with the query's heads resident (A operand). Work is
 //    laid over the flattened key rows, so ragged batches need no padding.
-//  * prefill kernel: many queries per sequence (chunked prefill). A workgroup owns 16 queries
-//    (4 per wave, A operands in registers) and walks the causal key range in 64-key tiles staged
-//    in LDS with direct global->LDS loads, double-buffered; each B fragment read from LDS feeds 4
-//    queries' MFMAs.
+//  * prefill kernel: many queries per sequence (chunked prefill). A workgroup of 8 waves owns 16
+//    queries (2 per wave, A operands in registers) and walks the causal key range in 64-key
+//    tiles staged in LDS by direct global->LDS loads through a 4-stage ring (three tiles load
+//    while one computes); each B fragment read from LDS feeds both of a wave's queries. Every
+//    tile issues the same number of memory operations (masked score stores go to a sink), so
+//    the ring is waited on with exact counts.
 #include <algorithm>
 
 #include "common.hpp"
