@@ -186,7 +186,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
   const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const __bf16* kvb = kv + qp.key_base * DQK;
-  float* xch = (float*)rbuf;                  // [8 waves][8][64]
+  float* xch = (float*)rbuf;                  // [8 waves][2][64 lanes][4]
   __bf16* pl = (__bf16*)rbuf;                 // [64 heads][P_STRIDE], after the exchange is read
 
   // Softmax with a fixed reference maximum per head: the first tile in which a head has a finite
@@ -384,30 +384,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       // kh is wave-uniform; both candidate elements are read at compile-time positions and made
       // opaque (an empty asm, no instruction) so the selects are not folded back into an indexed
       // register move
+      // The eight handed-over values of a lane go out as two 16-byte writes ([wave][half][lane]
+      // layout: each write is 64 lanes x 16 contiguous bytes, free of bank conflicts).
       float e0[8], e1[8];
+      f32x4 give[2];
 #pragma unroll
       for (int qi = 0; qi < 8; ++qi) {
         e0[qi] = s[kept_elem(qi, 0)];
         e1[qi] = s[kept_elem(qi, 1)];
         asm volatile("" : "+v"(e0[qi]), "+v"(e1[qi]));
-        xch[(wave * 8 + qi) * 64 + lane] = kh ? e0[qi] : e1[qi];
+        give[qi >> 2][qi & 3] = kh ? e0[qi] : e1[qi];
       }
+      f32x4* xch4 = reinterpret_cast<f32x4*>(xch);
+      xch4[(wave * 2 + 0) * 64 + lane] = give[0];
+      xch4[(wave * 2 + 1) * 64 + lane] = give[1];
       __syncthreads();
-      // the partner's eight values are all read before any is used (otherwise each read sinks
-      // into the branch of its row-validity test and the reads serialise)
-      float part[8];
-#pragma unroll
-      for (int qi = 0; qi < 8; ++qi) part[qi] = xch[((wave ^ 1) * 8 + qi) * 64 + lane];
-#pragma unroll
-      for (int qi = 0; qi < 8; ++qi) asm volatile("" : "+v"(part[qi]));
+      f32x4 part[2];
+      part[0] = xch4[((wave ^ 1) * 2 + 0) * 64 + lane];
+      part[1] = xch4[((wave ^ 1) * 2 + 1) * 64 + lane];
+      // Kept element qi of this lane is row r0 + 16*(qi/4) + qi%4 of the tile, r0 = 32*rb + 8*kh
+      // + 4*half: all eight validity bits come from one shift of the tile's mask.
+      const uint32_t vbits = (uint32_t)(vmask >> (32 * rb + 8 * kh + 4 * half));
       float sv[8];
       float mx = -INFINITY;
 #pragma unroll
       for (int qi = 0; qi < 8; ++qi) {
         const float mine = kh ? e1[qi] : e0[qi];
-        const float v = (mine + part[qi]) * scale_log2;
-        const int row = 32 * rb + mfma32_row(kept_elem(qi, kh), lane);
-        sv[qi] = ((vmask >> row) & 1) ? v : -INFINITY;
+        const float v = (mine + part[qi >> 2][qi & 3]) * scale_log2;
+        sv[qi] = ((vbits >> (16 * (qi >> 2) + (qi & 3))) & 1) ? v : -INFINITY;
         mx = fmaxf(mx, sv[qi]);
       }
       mx = halves_max(mx);                     // this wave's 16 rows, head c32 of its half
