@@ -40,6 +40,7 @@ constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / WAVE;
 constexpr int TK_BINS = 2048;
 constexpr int TK_HIST = TK_BINS + 64;          // bin TK_BINS collects NaN (never selected)
+constexpr int TK_OBUF = 2048;                  // k up to this is staged in LDS
 
 // The score whose key is k (inverse of score_key).
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -66,6 +67,7 @@ struct TopkShared {
   uint32_t red_c[TK_WAVES];            // wave exchanges of the compaction
   uint32_t red_d[TK_WAVES];
   uint32_t sel_bin, sel_need, sel_count, sel_min, sel_max;
+  int32_t obuf[TK_OBUF];               // selected positions, written out coalesced at the end
 };
 
 // Finds, in histogram h (bins 2*tid and 2*tid+1 per thread, keys counted from the top bin
@@ -124,6 +126,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const float* srow = scores + (int64_t)t * ld;
+  // The row is read in aligned 16-byte groups; `off` floats of the first group precede it.
+  // Positions fit in 32 bits (they are stored as int32).
+  const int off = (int)((reinterpret_cast<uintptr_t>(srow) >> 2) & 3);
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(srow - off);
+  const int lane_g = wave * SLICE4 + lane;       // group of unit 0 in chunk 0
+  const float qnan = __uint_as_float(0x7fc00000u);
+  // If the row's whole allocated span fits one register chunk, its loads go out before the
+  // sequence lookup (the row's address does not depend on it) and the visible length masks
+  // the values afterwards.
+  const int ng4_span = (int)((ld + off + 3) >> 2);
+  const bool early = ng4_span <= CHUNK4;
+  f32x4 pre[UNITS];
+  if (early) {
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) {
+      const int g = lane_g + u * WAVE;
+      pre[u] = g < ng4_span ? g4[g] : f32x4{qnan, qnan, qnan, qnan};
+    }
+  }
   const QueryPos qp = query_pos(cu_q, cu_k, nseq, total_k, t);
   const int64_t n = min(qp.p + 1, ld);           // visible positions 0..n-1 (0 if invalid)
   int32_t* orow = out + (int64_t)t * k;
@@ -131,16 +153,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     for (int i = tid; i < k; i += TK_THREADS) orow[i] = i < n ? i : -1;
     return;
   }
-  const float* srow = scores + (int64_t)t * ld;
-  // The row is read in aligned 16-byte groups; `off` floats of the first group precede it.
-  // Positions fit in 32 bits (they are stored as int32).
-  const int off = (int)((reinterpret_cast<uintptr_t>(srow) >> 2) & 3);
-  const f32x4* g4 = reinterpret_cast<const f32x4*>(srow - off);
   const int ni = (int)n;
   const int ng4 = (ni + off + 3) >> 2;
   const int nchunks = (ng4 + CHUNK4 - 1) / CHUNK4;
-  const int lane_g = wave * SLICE4 + lane;       // group of unit 0 in chunk 0
-  const float qnan = __uint_as_float(0x7fc00000u);
 
   float x[UNITS][4];
   // Unit u of this lane in chunk c is group c*CHUNK4 + lane_g + 64*u; its element e is
@@ -173,7 +188,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       }
     }
   };
-  if (nchunks == 1) load_chunk(0);
+  if (early) {
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = 4 * (lane_g + u * WAVE) + e - off;
+        x[u][e] = (pos >= 0 && pos < ni) ? pre[u][e] : qnan;
+      }
+  } else if (nchunks == 1) {
+    load_chunk(0);
+  }
 
   for (int i = tid; i < TK_HIST; i += TK_THREADS) {
     sh.hist[0][i] = 0;
@@ -310,7 +335,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     }
   } while (false);
 
-  // compaction in index order
+  // compaction in index order; with k <= TK_OBUF the positions are staged in LDS (every slot
+  // starts at -1) and written out with coalesced stores at the end
+  const bool staged = k <= TK_OBUF;
+  if (staged)
+    for (int i = tid; i < k; i += TK_THREADS) sh.obuf[i] = -1;
   uint32_t gt_chunk = 0, eq_chunk = 0;           // scores above / equal to thr in earlier chunks
   for_chunks([&](int c) {
     uint32_t gt = 0, eq = 0;
@@ -368,7 +397,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (tm[e] & lane_bit) {
-          if (slot < (uint32_t)k) orow[slot] = p0 + e;
+          if (slot < (uint32_t)k) {
+            if (staged) sh.obuf[slot] = p0 + e;
+            else orow[slot] = p0 + e;
+          }
           ++slot;
         }
       }
@@ -376,6 +408,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       for (int e = 0; e < 4; ++e) base += (uint32_t)__popcll(tm[e]);
     }
   });
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < k; i += TK_THREADS) orow[i] = sh.obuf[i];
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
