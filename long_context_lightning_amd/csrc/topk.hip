@@ -68,6 +68,8 @@ struct TopkShared {
   uint32_t red_d[TK_WAVES];
   uint32_t sel_bin, sel_need, sel_count, sel_min, sel_max;
   int32_t obuf[TK_OBUF];               // selected positions, written out coalesced at the end
+  float cand_val[TK_OBUF];             // candidates of a streamed row (scores, positions)
+  int32_t cand_pos[TK_OBUF];
 };
 
 // Finds, in histogram h (bins 2*tid and 2*tid+1 per thread, keys counted from the top bin
@@ -112,7 +114,9 @@ __device__ __forceinline__ uint32_t lin_bin(float x, float scale, float bias) {
   return x == x ? (uint32_t)fmaxf(f, 0.f) : (uint32_t)TK_BINS;
 }
 
-template <int UNITS>
+// MODE: 0 = every row fits one register chunk; 1 = longer rows streamed through the candidate
+// buffer (k <= TK_OBUF); 2 = longer rows re-read chunk by chunk on every pass.
+template <int UNITS, int MODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int k,
@@ -177,17 +181,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       }
     }
   };
-  // f(c) for every chunk with x[][] holding that chunk
-  auto for_chunks = [&](auto&& f) {
-    if (nchunks == 1) {
-      f(0);
-    } else {
-      for (int c = 0; c < nchunks; ++c) {
-        load_chunk(c);
-        f(c);
-      }
-    }
-  };
   if (early) {
 #pragma unroll
     for (int u = 0; u < UNITS; ++u)
@@ -196,59 +189,85 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
         const int pos = 4 * (lane_g + u * WAVE) + e - off;
         x[u][e] = (pos >= 0 && pos < ni) ? pre[u][e] : qnan;
       }
-  } else if (nchunks == 1) {
+  } else {
     load_chunk(0);
   }
 
-  for (int i = tid; i < TK_HIST; i += TK_THREADS) {
-    sh.hist[0][i] = 0;
-    sh.hist[1][i] = 0;
-  }
-  for (int i = tid; i < TK_BINS; i += TK_THREADS) {
-    sh.bmin[0][i] = ALL;
-    sh.bmin[1][i] = ALL;
-    sh.bmax[0][i] = 0u;
-    sh.bmax[1][i] = 0u;
-  }
+  // Rows longer than one chunk are streamed when k fits the candidate buffer: after each chunk
+  // only the top k of (earlier candidates, chunk) survive, ties at the threshold keeping their
+  // lowest positions, which is exactly the part of them the final selection can take. Thread i
+  // holds candidates CPT*i.. in index order (NaN past the count). Otherwise every pass re-reads
+  // the row chunk by chunk.
+  constexpr int CPT = TK_OBUF / TK_THREADS;
+  constexpr bool stream = MODE == 1;
+  constexpr bool resident = MODE != 2;           // x holds the whole current segment
+  float cv[CPT];
+  int32_t cp[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) { cv[j] = qnan; cp[j] = 0; }
 
-  // value range of the row (fminf / fmaxf skip NaN)
-  float xmin = __int_as_float(0x7f800000), xmax = -xmin;
-  for_chunks([&](int) {
+  // f(v) for every score of the current segment
+  auto visit = [&](auto&& f) {
+    auto regs = [&]() {
 #pragma unroll
-    for (int u = 0; u < UNITS; ++u)
+      for (int u = 0; u < UNITS; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xmin = fminf(xmin, x[u][e]);
-        xmax = fmaxf(xmax, x[u][e]);
+        for (int e = 0; e < 4; ++e) f(x[u][e]);
+    };
+    if constexpr (resident) {
+      regs();
+      if constexpr (stream)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) f(cv[j]);
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+        load_chunk(c);
+        regs();
       }
-  });
-  xmin = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(xmin), 0x7f800000u, MinF32())));
-  xmax = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(xmax), 0xff800000u, MaxF32())));
-  if (lane == 0) { sh.red_a[wave] = __float_as_uint(xmin); sh.red_b[wave] = __float_as_uint(xmax); }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w) {
-    xmin = fminf(xmin, __uint_as_float(sh.red_a[w]));
-    xmax = fmaxf(xmax, __uint_as_float(sh.red_b[w]));
-  }
+    }
+  };
 
-  // radix select
-  uint32_t need = (uint32_t)k;                   // scores to take from the current range
-  float thr = xmin;
-  uint32_t thr_need = need;
-  do {
-    if (!(xmin < xmax)) break;                   // a single value: take k of them
+  // The threshold T of the current segment and how many scores equal to T are taken (all of
+  // them when the result is ALL).
+  auto select = [&](float& thr, uint32_t& thr_need) {
+    for (int i = tid; i < TK_HIST; i += TK_THREADS) {
+      sh.hist[0][i] = 0;
+      sh.hist[1][i] = 0;
+    }
+    for (int i = tid; i < TK_BINS; i += TK_THREADS) {
+      sh.bmin[0][i] = ALL;
+      sh.bmin[1][i] = ALL;
+      sh.bmax[0][i] = 0u;
+      sh.bmax[1][i] = 0u;
+    }
+    // value range (fminf / fmaxf skip NaN)
+    float xmin = __int_as_float(0x7f800000), xmax = -xmin;
+    visit([&](float v) {
+      xmin = fminf(xmin, v);
+      xmax = fmaxf(xmax, v);
+    });
+    xmin = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(xmin), 0x7f800000u, MinF32())));
+    xmax = __uint_as_float(last_lane(wave_incl_scan(__float_as_uint(xmax), 0xff800000u, MaxF32())));
+    if (lane == 0) { sh.red_a[wave] = __float_as_uint(xmin); sh.red_b[wave] = __float_as_uint(xmax); }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+      xmin = fminf(xmin, __uint_as_float(sh.red_a[w]));
+      xmax = fmaxf(xmax, __uint_as_float(sh.red_b[w]));
+    }
+    __syncthreads();                             // red_a / red_b are reused by select_bin
+
+    uint32_t need = (uint32_t)k;                 // scores to take from the current range
+    thr = xmin;
+    thr_need = need;
+    if (!(xmin < xmax)) return;                  // a single value: take k of them
     // round 0: linear bins over [xmin, xmax]
     const float s0 = (float)TK_BINS / (xmax - xmin);
     uint32_t lo, hi, count;
     if (s0 > 0.f && s0 <= __FLT_MAX__) {         // finite range: xmin and xmax are finite
       const float c0 = -xmin * s0;
-      for_chunks([&](int) {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (x[u][e] == x[u][e]) atomicAdd(&sh.hist[0][lin_bin(x[u][e], s0, c0)], 1u);
+      visit([&](float v) {
+        if (v == v) atomicAdd(&sh.hist[0][lin_bin(v, s0, c0)], 1u);
       });
       __syncthreads();
       select_bin(sh.hist[0], sh.bmin[0], sh.bmax[0], need, sh);
@@ -259,20 +278,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       float c1 = -(xmin + (float)bin0 / s0) * s1;
       if (!(s1 <= __FLT_MAX__ && c1 <= __FLT_MAX__ && c1 >= -__FLT_MAX__)) { s1 = 0.f; c1 = 0.f; }
       for (int i = tid; i < TK_HIST; i += TK_THREADS) sh.hist[0][i] = 0;  // read in select_bin
-      for_chunks([&](int) {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = x[u][e];
-            if (lin_bin(v, s0, c0) == bin0) {
-              const uint32_t b = lin_bin(v, s1, c1);
-              const uint32_t kk = score_key(v);
-              atomicAdd(&sh.hist[1][b], 1u);
-              atomicMin(&sh.bmin[1][b], kk);
-              atomicMax(&sh.bmax[1][b], kk);
-            }
-          }
+      visit([&](float v) {
+        if (lin_bin(v, s0, c0) == bin0) {
+          const uint32_t b = lin_bin(v, s1, c1);
+          const uint32_t kk = score_key(v);
+          atomicAdd(&sh.hist[1][b], 1u);
+          atomicMin(&sh.bmin[1][b], kk);
+          atomicMax(&sh.bmax[1][b], kk);
+        }
       });
       __syncthreads();
       select_bin(sh.hist[1], sh.bmin[1], sh.bmax[1], need, sh);
@@ -311,20 +324,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
         sh.bmax[cur ^ 1][i] = 0u;
       }
       const float vlo = key_value(lo), vhi = key_value(hi);
-      for_chunks([&](int) {
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = x[u][e];
-            if (v >= vlo && v <= vhi) {
-              const uint32_t kk = score_key(v);
-              const uint32_t b = (kk - lo) >> shift;
-              atomicAdd(&hc[b], 1u);
-              atomicMin(&mn[b], kk);
-              atomicMax(&mx[b], kk);
-            }
-          }
+      visit([&](float v) {
+        if (v >= vlo && v <= vhi) {
+          const uint32_t kk = score_key(v);
+          const uint32_t b = (kk - lo) >> shift;
+          atomicAdd(&hc[b], 1u);
+          atomicMin(&mn[b], kk);
+          atomicMax(&mx[b], kk);
+        }
       });
       __syncthreads();
       select_bin(hc, mn, mx, need, sh);
@@ -333,15 +340,48 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       lo = sh.sel_min;
       hi = sh.sel_max;
     }
-  } while (false);
+  };
 
-  // compaction in index order; with k <= TK_OBUF the positions are staged in LDS (every slot
-  // starts at -1) and written out with coalesced stores at the end
-  const bool staged = k <= TK_OBUF;
-  if (staged)
-    for (int i = tid; i < k; i += TK_THREADS) sh.obuf[i] = -1;
-  uint32_t gt_chunk = 0, eq_chunk = 0;           // scores above / equal to thr in earlier chunks
-  for_chunks([&](int c) {
+  // Compaction in index order: a position is taken if its score is above thr, or equal to it
+  // and among the first thr_need such positions; the slot of a taken position is the number of
+  // positions taken before it. sink(slot, position, score) stores one taken position.
+  // The candidates of a streamed row come first (all their positions precede the chunk's).
+  auto compact_cands = [&](float thr, uint32_t thr_need, uint32_t& gt_tot, uint32_t& eq_tot,
+                           auto&& sink) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      gt += cv[j] > thr;
+      eq += cv[j] == thr;
+    }
+    const uint32_t igt = wave_incl_scan_u32(gt), ieq = wave_incl_scan_u32(eq);
+    if (lane == WAVE - 1) { sh.red_c[wave] = igt; sh.red_d[wave] = ieq; }
+    __syncthreads();
+    uint32_t gt_b = igt - gt, eq_b = ieq - eq;
+    gt_tot = 0;
+    eq_tot = 0;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+      const uint32_t a = sh.red_c[w], b = sh.red_d[w];
+      if (w < wave) { gt_b += a; eq_b += b; }
+      gt_tot += a;
+      eq_tot += b;
+    }
+    __syncthreads();                             // red_c / red_d are reused by the chunk
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      if (cv[j] > thr) {
+        sink(gt_b + min(eq_b, thr_need), cp[j], cv[j]);
+        ++gt_b;
+      } else if (cv[j] == thr) {
+        if (eq_b < thr_need) sink(gt_b + eq_b, cp[j], cv[j]);
+        ++eq_b;
+      }
+    }
+  };
+  // chunk c (x holding it); gt_chunk / eq_chunk count the scores above / equal to thr before it
+  auto compact_chunk = [&](int c, float thr, uint32_t thr_need, uint32_t& gt_chunk,
+                           uint32_t& eq_chunk, auto&& sink) {
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int u = 0; u < UNITS; ++u)
@@ -397,17 +437,75 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (tm[e] & lane_bit) {
-          if (slot < (uint32_t)k) {
-            if (staged) sh.obuf[slot] = p0 + e;
-            else orow[slot] = p0 + e;
-          }
+          if (slot < (uint32_t)k) sink(slot, p0 + e, x[u][e]);
           ++slot;
         }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) base += (uint32_t)__popcll(tm[e]);
     }
-  });
+  };
+
+  // with k <= TK_OBUF the output is staged in LDS (every slot starts at -1) and written out
+  // with coalesced stores at the end
+  const bool staged = k <= TK_OBUF;
+  auto out_sink = [&](uint32_t slot, int pos, float) {
+    if (staged) sh.obuf[slot] = pos;
+    else orow[slot] = pos;
+  };
+  if (staged)
+    for (int i = tid; i < k; i += TK_THREADS) sh.obuf[i] = -1;
+
+  float thr = 0.f;
+  uint32_t thr_need;
+  if constexpr (stream) {
+    for (int c = 0; c < nchunks; ++c) {
+      if (c > 0) {
+        // The k candidates are all >= the previous threshold, and a later score equal to it
+        // loses the tie to every candidate of that value: only scores above it can still be
+        // taken, so the rest are masked out of every pass of this segment.
+        const float prev = thr;
+        load_chunk(c);
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!(x[u][e] > prev)) x[u][e] = qnan;
+      }
+      select(thr, thr_need);
+      uint32_t gt_tot = 0, eq_tot = 0;
+      if (c + 1 < nchunks) {                     // the segment's top k become the candidates
+        auto cand_sink = [&](uint32_t slot, int pos, float v) {
+          sh.cand_val[slot] = v;
+          sh.cand_pos[slot] = pos;
+        };
+        if (c > 0) compact_cands(thr, thr_need, gt_tot, eq_tot, cand_sink);
+        compact_chunk(c, thr, thr_need, gt_tot, eq_tot, cand_sink);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const int i = CPT * tid + j;
+          cv[j] = i < k ? sh.cand_val[i] : qnan;
+          cp[j] = i < k ? sh.cand_pos[i] : 0;
+        }
+        __syncthreads();                         // the buffer is rewritten by the next segment
+      } else {
+        compact_cands(thr, thr_need, gt_tot, eq_tot, out_sink);
+        compact_chunk(c, thr, thr_need, gt_tot, eq_tot, out_sink);
+      }
+    }
+  } else {
+    select(thr, thr_need);
+    uint32_t gt_chunk = 0, eq_chunk = 0;         // scores above / equal to thr in earlier chunks
+    if constexpr (MODE == 0) {
+      compact_chunk(0, thr, thr_need, gt_chunk, eq_chunk, out_sink);
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+        load_chunk(c);
+        compact_chunk(c, thr, thr_need, gt_chunk, eq_chunk, out_sink);
+      }
+    }
+  }
   if (staged) {
     __syncthreads();
     for (int i = tid; i < k; i += TK_THREADS) orow[i] = sh.obuf[i];
@@ -1044,11 +1142,11 @@ hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, 
   return hipGetLastError();
 }
 
-template <int UNITS>
+template <int UNITS, int MODE>
 hipError_t launch_rows(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        hipStream_t stream) {
-  topk_rows<UNITS><<<b.total_q, TK_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
-                                                         b.total_q, b.total_k, k, indices);
+  topk_rows<UNITS, MODE><<<b.total_q, TK_THREADS, 0, stream>>>(
+      scores, ld, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k, k, indices);
   return hipGetLastError();
 }
 
@@ -1066,10 +1164,12 @@ hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, i
   const int64_t longest = std::min<int64_t>(b.max_k, ld);
   const bool aligned = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && ld % 4 == 0;
   const int64_t groups = (longest + 3) / 4 + (aligned ? 0 : 1);
-  if (groups <= 1 * TK_THREADS) return launch_rows<1>(b, scores, ld, k, indices, stream);
-  if (groups <= 2 * TK_THREADS) return launch_rows<2>(b, scores, ld, k, indices, stream);
-  if (groups <= 4 * TK_THREADS) return launch_rows<4>(b, scores, ld, k, indices, stream);
-  return launch_rows<8>(b, scores, ld, k, indices, stream);
+  if (groups <= 1 * TK_THREADS) return launch_rows<1, 0>(b, scores, ld, k, indices, stream);
+  if (groups <= 2 * TK_THREADS) return launch_rows<2, 0>(b, scores, ld, k, indices, stream);
+  if (groups <= 4 * TK_THREADS) return launch_rows<4, 0>(b, scores, ld, k, indices, stream);
+  if (groups <= 8 * TK_THREADS) return launch_rows<8, 0>(b, scores, ld, k, indices, stream);
+  if (k <= TK_OBUF) return launch_rows<8, 1>(b, scores, ld, k, indices, stream);
+  return launch_rows<8, 2>(b, scores, ld, k, indices, stream);
 }
 
 }  // namespace dsa

@@ -420,6 +420,16 @@ def test_topk_many_long_rows():
     _crafted_topk(rows, 2048)
 
 
+def test_topk_many_long_rows_large_k():
+    """Rows longer than one register chunk with k above the candidate buffer: every pass
+    re-reads the row chunk by chunk."""
+    rng = np.random.default_rng(11)
+    rows = [rng.integers(-5, 6, int(n)).astype(np.float32)
+            for n in rng.integers(33000, 45000, 66)]
+    rows[5] = rng.normal(size=rows[5].shape[0]).astype(np.float32)
+    _crafted_topk(rows, 3000)
+
+
 def test_topk_split_rows_mixed_lengths():
     """A few long rows with short and dense rows beside them (the split-row path)."""
     rng = np.random.default_rng(10)
