@@ -20,6 +20,7 @@
 //    tile issues the same number of memory operations (masked score stores go to a sink), so
 //    the ring is waited on with exact counts.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -41,12 +42,17 @@ constexpr int DEC_STEP = 32;            // keys per MFMA step
 // Streams key rows s_beg, s_beg + stride, .. (32-key steps) of one sequence for query t, below
 // s_end. Each lane loads the 256-byte row of its key column straight into registers (the B
 // operand), two steps ahead of the MFMAs, so about 16 KB per wave are in flight.
+// With `preloaded`, b0..b2 already hold the first three steps' rows (loaded by flattened row
+// before the sequence lookup: rows past the sequence belong to the next one, and their scores
+// are computed but never stored).
 template <int HB>
 __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
                                                const __bf16* __restrict__ k_idx,
                                                const float* __restrict__ w, int t, int64_t kb0,
                                                int64_t s_beg, int64_t s_end,
-                                               float* __restrict__ srow, int stride) {
+                                               float* __restrict__ srow, int stride,
+                                               bool preloaded, bf16x8 (&b0)[8], bf16x8 (&b1)[8],
+                                               bf16x8 (&b2)[8]) {
   constexpr int HI = 32 * HB;
   const int lane = lane_id();
   const int half = lane >> 5;
@@ -85,11 +91,12 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
   };
   // three buffers with fixed register names (a rotating copy would wait for the loads), so
   // two steps of key rows stay in flight while one is multiplied
-  bf16x8 b0[8], b1[8], b2[8];
   if (s_beg >= s_end) return;
-  load(s_beg, b0);
-  load(min(s_beg + stride, s_end - 1), b1);
-  load(min(s_beg + 2 * stride, s_end - 1), b2);
+  if (!preloaded) {
+    load(s_beg, b0);
+    load(min(s_beg + stride, s_end - 1), b1);
+    load(min(s_beg + 2 * stride, s_end - 1), b2);
+  }
   for (int64_t s0 = s_beg; s0 < s_end; s0 += 3 * stride) {
     step(s0, b0);
     if (s0 + stride >= s_end) break;
@@ -110,27 +117,65 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
     float* __restrict__ scores, int64_t ld) {
   const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
   const int j = blockIdx.y;
   int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
   const int64_t f_end = min(f + DEC_KEYS_PER_BLOCK, total_k);
-  while (f < f_end) {
-    const int b = find_seq_wave(cu_k, nseq, f);
-    const int64_t kb0 = cu_k[b];
-    const int64_t kb1 = min(cu_k[b + 1], total_k);
-    if (kb1 <= f || kb0 > f) break;
+  // The first three steps' key rows of this wave, by flattened row: their addresses do not
+  // depend on the sequence lookup, so they load while it runs.
+  bf16x8 b0[8], b1[8], b2[8];
+  {
+    const __bf16* kr = k_idx + (lane >> 5) * 8;
+    auto pre = [&](int64_t r, bf16x8* dst) {
+      r = min(r, total_k - 1);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) dst[st] = *(const bf16x8*)(kr + r * D + st * 16);
+    };
+    const int64_t r0 = f + DEC_STEP * wave + (lane & 31);
+    pre(r0, b0);
+    pre(r0 + DEC_STEP * DEC_WAVES, b1);
+    pre(r0 + 2 * DEC_STEP * DEC_WAVES, b2);
+  }
+  // One segment: the rows of the workgroup's range that belong to the sequence of row f.
+  // Returns the first row past it, or f_end if the range cannot continue.
+  auto segment = [&](auto preloaded) -> int64_t {
+    // one round trip: lane i loads both boundaries of sequence base+i from cu_k and cu_q, the
+    // ballot over cu_k finds the sequence of row f, its boundaries come from that lane
+    int64_t kb0 = 0, kb1 = 0;
+    int q0 = 0, q1 = 0;
+    for (int base = 0;; base += WAVE) {
+      const int i = min(base + lane, max(nseq - 1, 0));
+      int64_t ka = cu_k[i], kz = cu_k[i + 1];
+      int32_t qa = cu_q[i], qz = cu_q[i + 1];
+      asm volatile("" : "+v"(ka), "+v"(kz), "+v"(qa), "+v"(qz));
+      const bool le = base + lane + 1 < nseq && kz <= f;
+      const int cnt = __popcll(__ballot(le));
+      if (cnt == WAVE) continue;
+      kb0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(ka >> 32), cnt) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)ka, cnt));
+      kb1 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kz >> 32), cnt) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)kz, cnt));
+      q0 = __builtin_amdgcn_readlane(qa, cnt);
+      q1 = __builtin_amdgcn_readlane(qz, cnt);
+      break;
+    }
+    kb1 = min(kb1, total_k);
+    if (kb1 <= f || kb0 > f) return f_end;
     const int64_t seg_end = min(f_end, kb1);
-    const int q0 = cu_q[b];
-    const int nq = cu_q[b + 1] - q0;
+    const int nq = q1 - q0;
     if (j < nq && q0 + j < total_q && q0 + j >= 0) {
       const int t = q0 + j;
       const int64_t p = (kb1 - kb0) - nq + j;
       const int64_t s_beg = f - kb0;
       const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
       decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg + DEC_STEP * wave, s_end,
-                         scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES);
+                         scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES, decltype(preloaded)::value,
+                         b0, b1, b2);
     }
-    f = seg_end;
-  }
+    return seg_end;
+  };
+  f = segment(std::true_type{});                 // usually the whole range
+  while (f < f_end) f = segment(std::false_type{});
 }
 
 constexpr int PF_QW = 2;                // queries per wave
