@@ -77,11 +77,23 @@ def mla_bytes(case):
     return tot
 
 
+def code_digest(path):
+    """SHA-256 of a kernel source with // comments, trailing blanks and empty lines removed: a
+    change of comments alone does not change the kernel the counters measured."""
+    import hashlib
+    import re
+    lines = []
+    for ln in open(path, encoding="utf-8"):
+        ln = re.sub(r"//.*$", "", ln.rstrip("\n")).rstrip()
+        if ln:
+            lines.append(ln)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def traffic_record(workload, kernel):
     """HBM bytes per launch of `kernel` measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
     from the committed summary profiles/<workload>_hbm_traffic.md; None when the summary is
-    missing or any kernel source changed since the counters were taken."""
-    import hashlib
+    missing or any kernel source's code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -92,10 +104,11 @@ def traffic_record(workload, kernel):
     if rec is None:
         return None
     csrc = os.path.join(ROOT, "long_context_lightning_amd", "csrc")
-    for name, sha in rec["sources_sha256"].items():
-        with open(os.path.join(csrc, name), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != sha:
-                return None
+    for name, sha in rec.get("code_sha256", {}).items():
+        if code_digest(os.path.join(csrc, name)) != sha:
+            return None
+    if "code_sha256" not in rec:
+        return None
     key = "traffic_bytes_per_launch" if kernel == rec["kernel"] else f"{kernel}_traffic_bytes_per_launch"
     return rec.get(key)
 

@@ -247,6 +247,18 @@ def test_index_heads_64_and_attention_heads_128():
     check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
 
 
+@pytest.mark.parametrize("heads", [32, 96])
+def test_attention_heads_odd_number_of_32_head_groups(heads):
+    """The last 64-head workgroup has an empty upper half (it computes on other heads' queries
+    and writes nothing); split and single-split launches."""
+    case = _small_case(f"heads{heads}", (5000, 700, 3100), (1, 1, 2), n_heads=heads)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    assert out.shape[1] == heads
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+
+
 def test_all_equal_scores_take_lowest_positions():
     case = _small_case("ties", (9000, 3000), (1, 2))
     d = DI.make_inputs(case, "cuda")
