@@ -244,6 +244,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         __builtin_amdgcn_sched_barrier(0);   // keep the groups apart: bounded live registers
       }
     };
+    // gather number jj (of LOADS_PER_THREAD) of a tile into stage `stg`; idxv already masked
+    auto issue_one = [&](char* stg, int idxv, int jj) __attribute__((always_inline)) {
+      const int sbase = jj * NTHREADS + wave * 64;                     // wave-uniform
+      const int r0 = sbase / CHUNKS;
+      const int slot = sbase + lane;
+      const int row = slot / CHUNKS;
+      const int gc = (slot - row * CHUNKS) ^ swz(row);
+      const int i0 = __builtin_amdgcn_readlane(idxv, r0);
+      const int i1 = __builtin_amdgcn_readlane(idxv, min(r0 + 1, TILE - 1));
+      const int vi = row == r0 ? i0 : i1;
+      const uint32_t v = (uint32_t)vi < Lu ? (uint32_t)vi : 0u;
+      gather16(kvb + (size_t)v * DQK + gc * 8, stg + sbase * 16);
+    };
     // Double buffering: tile j computes in stage j%2 while the gathers of tile j+1 stream into
     // the other stage. The indices of tile j+2 are loaded at the top of tile j (into the
     // register that held tile j's). At the end of tile j each wave waits for all its memory
@@ -363,8 +376,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     };
 
     // One tile in stage `stage`; idx holds the indices of this tile and receives those of
-    // tile+2, vm the row-validity mask of this tile and then of tile+2.
-    auto step = [&](char* stage, int tile, int& idx, uint64_t& vm) __attribute__((always_inline)) {
+    // tile+2, vm the row-validity mask of this tile and then of tile+2. The gathers of tile+1
+    // (into `other`, freed by the barrier that ended the previous tile) are issued here,
+    // spread over the QK^T steps, so their address arithmetic hides behind the matrix core;
+    // idx_next holds tile+1's indices.
+    auto step = [&](char* stage, char* other, int tile, int& idx, uint64_t& vm, int idx_next)
+        __attribute__((always_inline)) {
       const uint64_t vmask = vm;
       idx = load_idx(tile + 2);
 
@@ -373,11 +390,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       {
         bf16x8 a[2];
         auto rd = [&](int i, int b) __attribute__((always_inline)) { a[b] = *(const bf16x8*)(stage + abase[i & 3] + (i >> 2) * 128); };
+        static_assert(2 * LOADS_PER_THREAD == QK_STEPS, "one gather per two QK steps");
         rd(0, 0);
+        if (tile >= 1 && tile + 1 < ntiles) {    // uniform
+          const int idxv = masked(tile + 1, idx_next);
 #pragma unroll
-        for (int i = 0; i < QK_STEPS; ++i) {
-          if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
-          s = mfma32x32x16(a[i & 1], qreg[i], s);
+          for (int i = 0; i < QK_STEPS; ++i) {
+            if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
+            s = mfma32x32x16(a[i & 1], qreg[i], s);
+            if ((i & 1) == 0) issue_one(other, idxv, i >> 1);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < QK_STEPS; ++i) {
+            if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
+            s = mfma32x32x16(a[i & 1], qreg[i], s);
+          }
         }
       }
       // ---- exchange half sums: keep element set kh, hand the other to the partner wave
@@ -479,11 +507,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       wait_all_memory();
       vm = __ballot((uint32_t)masked(tile + 2, idx) < Lu);
       __syncthreads();
-      if (tile + 2 < ntiles) issue(stage, tile + 2, idx);
     };
     for (int tile = 0; tile < ntiles; tile += 2) {   // unrolled by two: each step names its stage
-      step(stage0, tile, i_even, vm_even);
-      if (tile + 1 < ntiles) step(stage1, tile + 1, i_odd, vm_odd);
+      step(stage0, stage1, tile, i_even, vm_even, i_odd);
+      if (tile + 1 < ntiles) step(stage1, stage0, tile + 1, i_odd, vm_odd, i_even);
     }
     wait_all_memory();
   }

@@ -255,7 +255,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       xmin = fminf(xmin, __uint_as_float(sh.red_a[w]));
       xmax = fmaxf(xmax, __uint_as_float(sh.red_b[w]));
     }
-    __syncthreads();                             // red_a / red_b are reused by select_bin
 
     uint32_t need = (uint32_t)k;                 // scores to take from the current range
     thr = xmin;
