@@ -33,6 +33,13 @@ constexpr int D = 128;                  // index_head_dim on the bf16 path
 // max(x, 0). This file is compiled without IEEE NaN handling (no NaN reaches the indexer), so
 // fmaxf is a single v_max_f32 instead of a NaN-quieting v_max followed by the maximum.
 __device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.f); }
+
+// x of lanes l and l^32 added, in every lane, with one gfx950 lane-half swap (of its two
+// results one holds the low half of x in both halves, the other the high half).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 constexpr int DEC_KEYS_PER_WAVE = 256;
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
@@ -287,28 +294,76 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
                                (7 << 4) | (0 << 8));   // vmcnt(16), lgkmcnt(0)
     __syncthreads();                     // tile ti landed for every wave; tile ti-1 consumed
     issue(ti + PF_NST - 1);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int row = sub * 32 + col;
+    // the exact wait above counts this tile's loads before its stores: keep them in that order
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (HB == 1) {
+      // Four MFMA chains per tile, (sub, query) = (0,0) (0,1) (1,0) (1,1). Each chain's eight
+      // MFMAs are issued interleaved with the epilogue (ReLU, x w, head sum) of the previous
+      // chain, one MFMA to four VALU instructions, so the matrix core stays busy while the
+      // epilogue runs; two accumulators alternate.
       bf16x8 bop[8];
+      auto load_b = [&](int sub) {
+        const int row = sub * 32 + col;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int chunk = st * 2 + half;
-        bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
-      }
-#pragma unroll
-      for (int qi = 0; qi < PF_QW; ++qi) {
+        for (int st = 0; st < 8; ++st) {
+          const int chunk = st * 2 + half;
+          bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
+        }
+      };
+      auto epilogue = [&](int qi, const f32x16& acc) {
         float v = 0.f;
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          f32x16 acc = {};
+        for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][0][r], relu(acc[r]), v);
+        return v;
+      };
+      f32x16 acc[2];
+      float vs[4];
+      load_b(0);
+      acc[0] = f32x16{};
 #pragma unroll
-          for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[qi][hb][st], bop[st], acc);
+      for (int st = 0; st < 8; ++st) acc[0] = mfma32x32x16(a[0][0][st], bop[st], acc[0]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], relu(acc[r]), v);
+      for (int c = 1; c < 4; ++c) {
+        const int sub = c >> 1, qi = c & 1;
+        if (c == 2) load_b(1);
+        acc[c & 1] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          acc[c & 1] = mfma32x32x16(a[qi][0][st], bop[st], acc[c & 1]);
+        vs[c - 1] = epilogue((c - 1) & 1, acc[(c - 1) & 1]);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
         }
-        v += __shfl_xor(v, 32, WAVE);
-        store(ti, sub, qi, v);
+        (void)sub;
+      }
+      vs[3] = epilogue(1, acc[1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) store(ti, c >> 1, c & 1, halves_sum(vs[c]));
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = sub * 32 + col;
+        bf16x8 bop[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int chunk = st * 2 + half;
+          bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
+        }
+#pragma unroll
+        for (int qi = 0; qi < PF_QW; ++qi) {
+          float v = 0.f;
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[qi][hb][st], bop[st], acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], relu(acc[r]), v);
+          }
+          store(ti, sub, qi, halves_sum(v));
+        }
       }
     }
   }
