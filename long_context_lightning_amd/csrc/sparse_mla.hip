@@ -593,6 +593,8 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
                                                            float* __restrict__ lse) {
   extern __shared__ float wgt[];               // [nsplit][32] merge weights per head
   __shared__ float red[3][16][WAVE];           // partial sums of waves 1..3
+  __shared__ float mred[8][32], sred[8][32];   // per-head maximum / sum of eight threads
+  __shared__ __attribute__((aligned(16))) __bf16 ot[32][40];   // output block, row = head
   const int t = blockIdx.x;
   const int y = blockIdx.y;
   const int db = y % VB_WAVE;
@@ -622,18 +624,34 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
   for (int j = tid; j < nsplit * 32; j += CMB_THREADS)
     wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
   __syncthreads();
-  if (tid < 32) {
-    float mx = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, wgt[i * 32 + tid]);
+  // merge weights exp(lse_i - lse): eight threads per head, each over every eighth split, the
+  // maximum and the sum meeting in LDS (base-2 hardware exponent and logarithm)
+  {
+    const int hh = tid & 31, g = tid >> 5;
+    float m = -INFINITY;
+    for (int i = g; i < nsplit; i += 8) m = fmaxf(m, wgt[i * 32 + hh]);
+    mred[g][hh] = m;
+    __syncthreads();
+    m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, mred[j][hh]);
+    const float m2 = m * kLog2e;
     float sum = 0.f;
-    if (mx != -INFINITY)
-      for (int i = 0; i < nsplit; ++i) sum += expf(wgt[i * 32 + tid] - mx);
-    const float tot = (mx == -INFINITY) ? -INFINITY : mx + logf(sum);
-    for (int i = 0; i < nsplit; ++i) {
-      const float li = wgt[i * 32 + tid];
-      wgt[i * 32 + tid] = (li == -INFINITY) ? 0.f : expf(li - tot);
+    if (m != -INFINITY)
+      for (int i = g; i < nsplit; i += 8)
+        sum += __builtin_amdgcn_exp2f(wgt[i * 32 + hh] * kLog2e - m2);
+    sred[g][hh] = sum;
+    __syncthreads();
+    sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += sred[j][hh];
+    const float tot2 = m2 + __builtin_amdgcn_logf(sum);   // log2 units; sum >= 1
+    for (int i = g; i < nsplit; i += 8) {
+      const float li = wgt[i * 32 + hh];
+      wgt[i * 32 + hh] = (li == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(li * kLog2e - tot2);
     }
-    if (lse && w == 0 && db == 0) lse[(int64_t)t * H + h0 + tid] = tot;
+    if (lse && w == 0 && db == 0 && g == 0)
+      lse[(int64_t)t * H + h0 + hh] = (m == -INFINITY) ? -INFINITY : tot2 * kLn2;
   }
   __syncthreads();
   float acc[16];
@@ -661,11 +679,16 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
   }
   __syncthreads();
   if (wv == 0) {
-    __bf16* ob = out + ((int64_t)t * H + h0) * DV + (VB_WAVE * w + db) * 32 + (lane & 31);
+    // the [32 heads x 32 columns] block is transposed through LDS (in order within the wave),
+    // then each lane stores 32 contiguous bytes of one head's row
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      ob[(int64_t)mfma32_row(r, lane) * DV] =
+      ot[mfma32_row(r, lane)][lane & 31] =
           (__bf16)(acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane]);
+    const int row = lane >> 1, c0 = (lane & 1) * 16;
+    __bf16* ob = out + ((int64_t)t * H + h0 + row) * DV + (VB_WAVE * w + db) * 32 + c0;
+    *(bf16x8*)ob = *(const bf16x8*)&ot[row][c0];
+    *(bf16x8*)(ob + 8) = *(const bf16x8*)&ot[row][c0 + 8];
   }
 }
 
