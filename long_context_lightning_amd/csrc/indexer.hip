@@ -252,31 +252,60 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
     }
   }
 
-  // Stage layout: key row r occupies 16 slots of 16 B; the slot of 16-B chunk c is c ^ (r & 7),
-  // so the 32 rows read by one B-operand load spread over all LDS banks. Tiles past the range
+  // The tile loop runs on 32-bit wave-uniform tile numbers (scalar registers). Tiles below
+  // t_fast_ld have all 64 key rows in range; tiles below t_fast_st are in range and visible to
+  // every query of a full block: those take loads / stores addressed from a uniform base plus a
+  // constant per-lane offset, the others clamp and mask per lane.
+  const int tb = __builtin_amdgcn_readfirstlane((int)tile_beg);
+  const int te = __builtin_amdgcn_readfirstlane((int)tile_end);
+  const int t_fast_ld = __builtin_amdgcn_readfirstlane((int)min((int64_t)te, nkeys / PF_KT));
+  const int t_fast_st = __builtin_amdgcn_readfirstlane(
+      jcount == PF_QB ? (int)min((int64_t)te, min(p_first + 1, nkeys) / PF_KT) : 0);
+
+  // Stage layout: key row r occupies 16 slots of 16 B; the slot of 16-B chunk c is c ^ (r & 15),
+  // so any 16 consecutive rows read by one B-operand load use 16 distinct 16-byte bank groups. Tiles past the range
   // load key 0 into their (never read) stage so every iteration issues the same loads.
-  auto issue = [&](int64_t ti) {
-    const int stg = (int)(ti % PF_NST);
+  uint32_t ld_off[PF_LOADS];                   // byte offset of this lane's chunk in a tile
 #pragma unroll
-    for (int c = 0; c < PF_LOADS; ++c) {
-      const int slot = c * PF_THREADS + tid;
-      const int row = slot >> 4;
-      const int gc = (slot & 15) ^ (row & 7);
-      const int64_t key = ti < tile_end ? min(ti * PF_KT + row, nkeys - 1) : 0;
-      global_to_lds16(k_idx + (kb0 + key) * D + gc * 8,
-                      &ktile[stg][(c * PF_THREADS + wave * 64) * 8]);
+  for (int c = 0; c < PF_LOADS; ++c) {
+    const int slot = c * PF_THREADS + tid;
+    const int row = slot >> 4;
+    ld_off[c] = (uint32_t)(row * D + (((slot & 15) ^ (row & 15)) * 8)) * 2u;
+  }
+  auto issue = [&](int ti) {
+    const int stg = ti & (PF_NST - 1);
+    if (__builtin_expect(ti < t_fast_ld, 1)) {
+      const char* base = (const char*)(k_idx + (kb0 + (int64_t)ti * PF_KT) * D);
+#pragma unroll
+      for (int c = 0; c < PF_LOADS; ++c)
+        global_to_lds16(base + ld_off[c], &ktile[stg][(c * PF_THREADS + wave * 64) * 8]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < PF_LOADS; ++c) {
+        const int slot = c * PF_THREADS + tid;
+        const int row = slot >> 4;
+        const int gc = (slot & 15) ^ (row & 15);
+        const int64_t key = ti < te ? min((int64_t)ti * PF_KT + row, nkeys - 1) : 0;
+        global_to_lds16(k_idx + (kb0 + key) * D + gc * 8,
+                        &ktile[stg][(c * PF_THREADS + wave * 64) * 8]);
+      }
     }
   };
   // one store per (sub, qi) for every lane: both lane halves hold the finished score of key
   // `col` and write it to the same address; lanes without a score write to the sink
   float* sink = g_score_sink + (blockIdx.x % PF_SINKS) * (PF_STORES * WAVE) + lane;
-  auto store = [&](int64_t ti, int sub, int qi, float v) {
-    const int64_t s = ti * PF_KT + sub * 32 + col;
+  auto store = [&](auto fast, int ti, int sub, int qi, float v) {
     const int jq = jb + wave * PF_QW + qi;
-    const int64_t p = p_first + wave * PF_QW + qi;
-    const bool own = ti < tile_end && jq < nq && s <= p && s < nkeys;
-    float* dst = own ? scores + (int64_t)(q0 + jq) * ld + s : sink + (sub * PF_QW + qi) * WAVE;
-    __builtin_nontemporal_store(v, dst);
+    if constexpr (decltype(fast)::value) {
+      float* row = scores + (int64_t)(q0 + jq) * ld + (int64_t)ti * PF_KT;
+      __builtin_nontemporal_store(v, row + (sub * 32 + col));
+    } else {
+      const int64_t s = (int64_t)ti * PF_KT + sub * 32 + col;
+      const int64_t p = p_first + wave * PF_QW + qi;
+      const bool own = ti < te && jq < nq && s <= p && s < nkeys;
+      float* dst = own ? scores + (int64_t)(q0 + jq) * ld + s : sink + (sub * PF_QW + qi) * WAVE;
+      __builtin_nontemporal_store(v, dst);
+    }
   };
 
   // Issue order: the first PF_NST-1 tiles, a full wait, then per iteration [loads of tile
@@ -284,11 +313,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
   // PF_STORES memory operations follow the loads of the tile being waited for; in the first
   // three that tile has already landed.
 #pragma unroll
-  for (int j = 0; j < PF_NST - 1; ++j) issue(tile_beg + j);
+  for (int j = 0; j < PF_NST - 1; ++j) issue(tb + j);
   wait_all_memory();
 
-  for (int64_t ti = tile_beg; ti < tile_end; ++ti) {
-    const int stg = (int)(ti % PF_NST);
+  for (int ti = tb; ti < te; ++ti) {
+    const int stg = ti & (PF_NST - 1);
     __builtin_amdgcn_s_waitcnt((((PF_LOADS + PF_STORES) * 2 + PF_STORES) & 15) |
                                ((((PF_LOADS + PF_STORES) * 2 + PF_STORES) >> 4) << 14) |
                                (7 << 4) | (0 << 8));   // vmcnt(16), lgkmcnt(0)
@@ -300,47 +329,52 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
       // Four MFMA chains per tile, (sub, query) = (0,0) (0,1) (1,0) (1,1). Each chain's eight
       // MFMAs are issued interleaved with the epilogue (ReLU, x w, head sum) of the previous
       // chain, one MFMA to four VALU instructions, so the matrix core stays busy while the
-      // epilogue runs; two accumulators alternate.
-      bf16x8 bop[8];
-      auto load_b = [&](int sub) {
-        const int row = sub * 32 + col;
+      // epilogue runs; two accumulators alternate. The body is one basic block per tile kind
+      // (stores without per-lane masks, or masked), so the interleave is not cut by branches.
+      auto body = [&](auto fast) __attribute__((always_inline)) {
+        bf16x8 bop[2][8];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const int chunk = st * 2 + half;
-          bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
+        for (int sub = 0; sub < 2; ++sub) {
+          const int row = sub * 32 + col;
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            const int chunk = st * 2 + half;
+            bop[sub][st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 15))) * 8];
+          }
         }
-      };
-      auto epilogue = [&](int qi, const f32x16& acc) {
-        float v = 0.f;
+        auto epilogue = [&](int qi, const f32x16& acc) {
+          float v = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][0][r], relu(acc[r]), v);
-        return v;
-      };
-      f32x16 acc[2];
-      float vs[4];
-      load_b(0);
-      acc[0] = f32x16{};
+          for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][0][r], relu(acc[r]), v);
+          return v;
+        };
+        f32x16 acc[2];
+        float vs[4];
+        acc[0] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) acc[0] = mfma32x32x16(a[0][0][st], bop[st], acc[0]);
+        for (int st = 0; st < 8; ++st) acc[0] = mfma32x32x16(a[0][0][st], bop[0][st], acc[0]);
 #pragma unroll
-      for (int c = 1; c < 4; ++c) {
-        const int sub = c >> 1, qi = c & 1;
-        if (c == 2) load_b(1);
-        acc[c & 1] = f32x16{};
+        for (int c = 1; c < 4; ++c) {
+          const int sub = c >> 1, qi = c & 1;
+          acc[c & 1] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-          acc[c & 1] = mfma32x32x16(a[qi][0][st], bop[st], acc[c & 1]);
-        vs[c - 1] = epilogue((c - 1) & 1, acc[(c - 1) & 1]);
+          for (int st = 0; st < 8; ++st)
+            acc[c & 1] = mfma32x32x16(a[qi][0][st], bop[sub][st], acc[c & 1]);
+          vs[c - 1] = epilogue((c - 1) & 1, acc[(c - 1) & 1]);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+          for (int st = 0; st < 8; ++st) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+          }
         }
-        (void)sub;
-      }
-      vs[3] = epilogue(1, acc[1]);
+        vs[3] = epilogue(1, acc[1]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) store(ti, c >> 1, c & 1, halves_sum(vs[c]));
+        for (int c = 0; c < 4; ++c) store(fast, ti, c >> 1, c & 1, halves_sum(vs[c]));
+      };
+      if (__builtin_expect(ti < t_fast_st, 1))
+        body(std::true_type{});
+      else
+        body(std::false_type{});
     } else {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
@@ -349,7 +383,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
           const int chunk = st * 2 + half;
-          bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 7))) * 8];
+          bop[st] = *(const bf16x8*)&ktile[stg][(row * 16 + (chunk ^ (row & 15))) * 8];
         }
 #pragma unroll
         for (int qi = 0; qi < PF_QW; ++qi) {
@@ -362,7 +396,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
 #pragma unroll
             for (int r = 0; r < 16; ++r) v = fmaf(wr[qi][hb][r], relu(acc[r]), v);
           }
-          store(ti, sub, qi, halves_sum(v));
+          if (__builtin_expect(ti < t_fast_st, 1))
+            store(std::true_type{}, ti, sub, qi, halves_sum(v));
+          else
+            store(std::false_type{}, ti, sub, qi, halves_sum(v));
         }
       }
     }
