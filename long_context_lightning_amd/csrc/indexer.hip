@@ -361,11 +361,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
           for (int st = 0; st < 8; ++st)
             acc[c & 1] = mfma32x32x16(a[qi][0][st], bop[sub][st], acc[c & 1]);
           vs[c - 1] = epilogue((c - 1) & 1, acc[(c - 1) & 1]);
+        }
+        // schedule (one pattern for the whole body): chain 0 alone, then chains 1..3 with each
+        // MFMA followed by four epilogue instructions of the chain before it
 #pragma unroll
-          for (int st = 0; st < 8; ++st) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-          }
+        for (int st = 0; st < 8; ++st) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int st = 0; st < 24; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         vs[3] = epilogue(1, acc[1]);
 #pragma unroll
