@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--launch", choices=["eager", "graph"], default="eager",
-                    help="time steps launched kernel by kernel (default) or replayed from one "
-                         "HIP graph per input set")
+                    help="headline: steps launched kernel by kernel (default) or replayed from "
+                         "one HIP graph per input set; the other mode is timed too")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -75,6 +76,20 @@ def mla_bytes(case):
     for t, b, p, base in DI.query_rows(case):
         tot += min(case.index_topk, p + 1) * case.d_qk * 2 + case.n_heads * (case.d_qk + case.d_v) * 2
     return tot
+
+
+def indexer_flops(case):
+    """Multiply-adds of the causal score grid, counted as two FLOPs each."""
+    import dsa_inputs as DI
+    return sum(2 * case.index_n_heads * case.index_head_dim * (p + 1)
+               for (_, _, p, _) in DI.query_rows(case))
+
+
+def mla_flops(case):
+    """QK^T over d_qk and P.V over d_v for every head and selected row of one layer."""
+    import dsa_inputs as DI
+    return sum(2 * case.n_heads * (case.d_qk + case.d_v) * min(case.index_topk, p + 1)
+               for (_, _, p, _) in DI.query_rows(case))
 
 
 def code_digest(path):
@@ -134,16 +149,31 @@ def cpu_baseline(case, sets, budget_s):
         host.append((f(d["q_idx"][t]), f(d["k_idx"][base:base + p + 1]), f(d["w"][t]),
                      f(d["q"][0][t]), f(d["kv"][0][base:base + p + 1])))
     done, spent = 0, 0.0
+    stage = [0.0, 0.0, 0.0]
     while spent < budget_s and done < 100000:
         qI, kI, w, q, kv = host[done % len(host)]
         t0 = time.perf_counter()
         s = O.indexer_scores_row(qI, kI, w)
+        t1 = time.perf_counter()
         sel = O.topk_row(s, case.index_topk)
+        t2 = time.perf_counter()
         O.sparse_attention_row(q, kv[sel[sel >= 0]], case.d_v, case.softmax_scale)
-        spent += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        stage = [stage[0] + t1 - t0, stage[1] + t2 - t1, stage[2] + t3 - t2]
+        spent += t3 - t0
         done += 1
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": done / spent, "unit": "query-tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "stage_seconds": {"indexer": round(stage[0], 3), "topk": round(stage[1], 3),
+                              "attention": round(stage[2], 3)},
             "sample": f"{done} decode queries of the same workload (full indexer over "
                       f"{max(case.seqlens_k)} keys, top-{case.index_topk}, {case.n_heads}-head "
                       f"sparse attention; {len(host)} distinct queries cycled), float64 NumPy, "
@@ -214,10 +244,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # --launch graph: one HIP graph per input set holds the step's kernels (same kernels, same
-    # arguments), replayed in the timed region.
+    # HIP graphs: one per input set holds the step's kernels (same kernels, same arguments)
     graphs = []
-    if args.launch == "graph":
+    if args.launch == "graph" or not args.no_graph:
         for i in range(nsets):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -227,16 +256,32 @@ def main():
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
 
-    # timed region 1: the headline, K whole steps
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[(args.warmup + i) % nsets].replay()
-        else:
-            step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    def time_steps(use_graphs):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if use_graphs:
+                graphs[(args.warmup + i) % nsets].replay()
+            else:
+                step(args.warmup + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # timed region 1: the headline, K whole steps, in both launch modes
+    ms_eager = time_steps(False)
+    ms_graph = time_steps(True) if graphs else None
+    ms_step = ms_graph if args.launch == "graph" else ms_eager
+    graph_info = None
+    if graphs:
+        # a replay must reproduce the eager step bit for bit (same kernels, same inputs)
+        step(0)
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs] + [idx.clone()]
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(ref, list(outs) + [idx]))
+        graph_info = {"ms_per_step": round(ms_graph, 5), "value": round(T / (ms_graph * 1e-3), 1),
+                      "replay_matches_eager": bool(same)}
 
     # timed region 2: the same K steps launched kernel by kernel, with HIP events on the launch
     # stream around every call (per-kernel durations and the roofline)
@@ -247,7 +292,9 @@ def main():
     ms_idx = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     ms_topk = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms_mla = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    ms_gpu = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
+    ms_gpu = sum(per_step) / args.steps
+    pct = lambda q: per_step[min(len(per_step) - 1, int(q * len(per_step)))]
 
     # timed region 3: each call's average launch duration, K launches back to back between two
     # events on the launch stream (region 2's events between the calls add their own gaps)
@@ -289,12 +336,22 @@ def main():
     kern = {"indexer": (launch_ms["indexer"], ib), "sparse_mla": (launch_ms["sparse_mla"], mb)}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
-    achieved = dbytes / (dms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
-            "algorithmic_bytes_per_launch": dbytes,
-            "avg_launch_ms": round(dms, 5)}
+    if max(case.seqlens_q) > 1 and case.dtype == torch.bfloat16:
+        # prefill: many queries share each key row, so the calls are matrix-core bound
+        dflops = indexer_flops(case) if dom == "indexer" else mla_flops(case)
+        achieved = dflops / (dms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
+                "algorithmic_flops_per_launch": dflops, "avg_launch_ms": round(dms, 5)}
+    else:
+        achieved = dbytes / (dms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
+                "algorithmic_bytes_per_launch": dbytes,
+                "avg_launch_ms": round(dms, 5)}
     line = {
         "metric": "DSA decode query-tokens/s + achieved HBM GB/s (indexer+top-k+sparse MLA)",
         "value": round(T / (ms_step * 1e-3), 1),
@@ -311,12 +368,16 @@ def main():
                                f"{case.n_heads}-head MQA over {case.d_qk}-wide latent "
                                f"({case.d_v} value), {case.layers} layer(s) per index pass",
                    "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets,
-                   "launch": "hip_graph" if graphs else "eager"},
+                   "launch": "hip_graph" if args.launch == "graph" else "eager"},
+        "eager_ms_per_step": round(ms_eager, 5),
+        "graph": graph_info,
         "achieved_hbm_gbps": round(sb / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": sb,
         "kernel_ms": {"indexer": round(ms_idx, 5), "topk": round(ms_topk, 5),
                       "sparse_mla_incl_merge": round(ms_mla, 5), "gpu_step": round(ms_gpu, 5),
-                      "timing": "events between the calls of every step"},
+                      "timing": "events between the calls of every step",
+                      "gpu_step_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5),
+                                               round(pct(0.9), 5)]},
         "launch_ms_back_to_back": {k: round(v, 5) for k, v in launch_ms.items()},
         "roofline": roof,
     }

@@ -156,6 +156,19 @@ def test_decode_forward_matches_separate_calls():
     assert torch.equal(i1, i3) and torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def test_multi_query_decode_full_size():
+    """Two to four new query tokens per sequence (speculative / multi-token decode) at the
+    decode sizes: 16 sequences of 16384 tokens, top-2048, 64 heads; every row checked."""
+    nq = (2, 3, 4, 2, 3, 4, 2, 3, 4, 2, 3, 4, 2, 3, 4, 2)
+    case = _small_case("mtp_b16_l16k", (16384,) * 16, nq)
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+
+
 @pytest.mark.slow
 def test_prefill_chunk8k_l64k_sampled():
     case = DI.CASES["prefill_chunk8k_l64k"]
