@@ -244,16 +244,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         __builtin_amdgcn_sched_barrier(0);   // keep the groups apart: bounded live registers
       }
     };
-    // gather number jj (of LOADS_PER_THREAD) of a tile into stage `stg`; idxv already masked
-    auto issue_one = [&](char* stg, int idxv, int jj) __attribute__((always_inline)) {
+    // gather number jj (of LOADS_PER_THREAD) of a tile into stage `stg`, for the index vi of
+    // the tile row this lane's slot lies in (fetched beforehand with one cross-lane read)
+    auto issue_one = [&](char* stg, int vi, int jj) __attribute__((always_inline)) {
       const int sbase = jj * NTHREADS + wave * 64;                     // wave-uniform
-      const int r0 = sbase / CHUNKS;
-      const int slot = sbase + lane;
+      const int slot = jj * NTHREADS + tid;
       const int row = slot / CHUNKS;
       const int gc = (slot - row * CHUNKS) ^ swz(row);
-      const int i0 = __builtin_amdgcn_readlane(idxv, r0);
-      const int i1 = __builtin_amdgcn_readlane(idxv, min(r0 + 1, TILE - 1));
-      const int vi = row == r0 ? i0 : i1;
       const uint32_t v = (uint32_t)vi < Lu ? (uint32_t)vi : 0u;
       gather16(kvb + (size_t)v * DQK + gc * 8, stg + sbase * 16);
     };
@@ -394,11 +391,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         rd(0, 0);
         if (tile >= 1 && tile + 1 < ntiles) {    // uniform
           const int idxv = masked(tile + 1, idx_next);
+          // the index of each gather's tile row, read across lanes (lane r holds row r's)
+          int vsel[LOADS_PER_THREAD];
+#pragma unroll
+          for (int jj = 0; jj < LOADS_PER_THREAD; ++jj)
+            vsel[jj] = __builtin_amdgcn_ds_bpermute(((jj * NTHREADS + tid) / CHUNKS) * 4, idxv);
 #pragma unroll
           for (int i = 0; i < QK_STEPS; ++i) {
             if (i + 1 < QK_STEPS) rd(i + 1, (i + 1) & 1);
             s = mfma32x32x16(a[i & 1], qreg[i], s);
-            if ((i & 1) == 0) issue_one(other, idxv, i >> 1);
+            if ((i & 1) == 0) issue_one(other, vsel[i >> 1], i >> 1);
           }
         } else {
 #pragma unroll
