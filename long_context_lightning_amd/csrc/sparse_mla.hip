@@ -763,7 +763,9 @@ MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
   const int64_t wgs = (int64_t)b.total_q * ((n_heads + WG_HEADS - 1) / WG_HEADS);
   const int64_t wgs1 = wgs > 0 ? wgs : 1;
   int nsplit = (int)((256 + wgs1 - 1) / wgs1);          // one workgroup per CU
-  nsplit = std::max(1, std::min(nsplit, tiles));
+  // at least two tiles per split: a split's first tile waits out the whole gather latency, its
+  // second tile's gathers overlap the first's compute, and every split adds a partial to merge
+  nsplit = std::max(1, std::min(nsplit, (tiles + 1) / 2));
   const int tiles_per_split = (tiles + nsplit - 1) / nsplit;
   p.rows_per_split = tiles_per_split * TILE;
   p.nsplit = (k + p.rows_per_split - 1) / p.rows_per_split;
