@@ -6,8 +6,8 @@ A step is one pass of the whole path over one batch: lightning indexer -> causal
 sparse MLA (plus the split-KV merge), on the decode workload of 32 sequences with 16384-token
 contexts, one new query each (indexer 32 heads x 128, top-k 2048, 64-head MQA over 576-wide
 bf16 latent rows). Inputs are seeded synthetic tensors resident in HBM before timing starts.
-Steps rotate over several independent input sets whose total size exceeds the 256 MB
-Infinity Cache, so a step cannot be served from the previous step's cached lines.
+Steps rotate over independent input sets: between two uses of one set the others touch at
+least 1 GiB (four times the 256 MB Infinity Cache), so a step is not served from cached lines.
 
 The timed steps launch their four kernels back to back on one stream; --launch graph replays
 one captured HIP graph per input set instead (slower here). Prints one JSON line: metric, value
@@ -192,8 +192,11 @@ def main():
 
     torch.cuda.set_device(0)
     case = DI.CASES[args.workload]
-    set_bytes = (case.total_k * (case.index_head_dim + case.d_qk * case.layers) * 2)
-    nsets = args.sets or max(2, math.ceil((1 << 30) / set_bytes))
+    # A step touches step_bytes(case) of its input set (the whole indexer key cache, only the
+    # selected latent rows). Between two uses of one set the other sets touch at least 1 GiB,
+    # four times the Infinity Cache, so no step is served from an earlier step's cached lines.
+    touched = step_bytes(case)
+    nsets = args.sets or max(2, 1 + math.ceil((1 << 30) / touched))
     sets = []
     for i in range(nsets):
         c = DI.Case(**{**case.__dict__, "seed_base": case.seed_base + 100 * i})
