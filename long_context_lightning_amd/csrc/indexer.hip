@@ -47,8 +47,8 @@ constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
 constexpr int DEC_STEP = 32;            // keys per MFMA step
 
 // Streams key rows s_beg, s_beg + stride, .. (32-key steps) of one sequence for query t, below
-// s_end. Each lane loads the 256-byte row of its key column straight into registers (the B
-// operand), two steps ahead of the MFMAs, so about 16 KB per wave are in flight.
+// s_end. Each step's 32 key rows (8 KB) are loaded into registers two steps ahead of the MFMAs,
+// so about 16 KB per wave are in flight, and pass through LDS into the B-operand layout.
 // With `preloaded`, b0..b2 already hold the first three steps' rows (loaded by flattened row
 // before the sequence lookup: rows past the sequence belong to the next one, and their scores
 // are computed but never stored).
@@ -59,7 +59,7 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
                                                int64_t s_beg, int64_t s_end,
                                                float* __restrict__ srow, int stride,
                                                bool preloaded, bf16x8 (&b0)[8], bf16x8 (&b1)[8],
-                                               bf16x8 (&b2)[8]) {
+                                               bf16x8 (&b2)[8], bf16x8* __restrict__ xw) {
   constexpr int HI = 32 * HB;
   const int lane = lane_id();
   const int half = lane >> 5;
@@ -76,13 +76,27 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
     for (int r = 0; r < 16; ++r) wr[hb][r] = w[(int64_t)t * HI + hb * 32 + mfma32_row(r, lane)];
   }
 
-  const __bf16* kb = k_idx + kb0 * D + half * 8;
+  // Key rows are read coalesced: load st of a step covers rows 4*st .. 4*st+3 of its 32, lane l
+  // the 16-byte chunk l%16 of row 4*st + l/16. One pass through this wave's LDS region turns
+  // them into the B operand (lane (col, half) of MFMA step st: chunk 2*st+half of row col);
+  // chunk c of row r sits in slot c ^ (r mod 16), so both passes are free of bank conflicts.
+  const __bf16* kb = k_idx + kb0 * D + (lane & 15) * 8;
   auto load = [&](int64_t s0, bf16x8* dst) {
-    const int64_t s = min(s0 + col, s_end - 1);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) dst[st] = *(const bf16x8*)(kb + s * D + st * 16);
+    for (int st = 0; st < 8; ++st) {
+      const int64_t s = min(s0 + 4 * st + (lane >> 4), s_end - 1);
+      dst[st] = *(const bf16x8*)(kb + s * D);
+    }
   };
-  auto step = [&](int64_t s0, const bf16x8* bop) {
+  auto step = [&](int64_t s0, const bf16x8* rows) {
+    bf16x8 bop[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int r = 4 * st + (lane >> 4);
+      xw[r * 16 + ((lane & 15) ^ (r & 15))] = rows[st];
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) bop[st] = xw[col * 16 + ((2 * st + half) ^ (col & 15))];
     float v = 0.f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -123,6 +137,7 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     const float* __restrict__ w, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
     float* __restrict__ scores, int64_t ld) {
+  __shared__ bf16x8 xbuf[DEC_WAVES][DEC_STEP * 16];   // one step of key rows per wave
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int j = blockIdx.y;
@@ -132,13 +147,13 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   // depend on the sequence lookup, so they load while it runs.
   bf16x8 b0[8], b1[8], b2[8];
   {
-    const __bf16* kr = k_idx + (lane >> 5) * 8;
+    const __bf16* kr = k_idx + (lane & 15) * 8;
     auto pre = [&](int64_t r, bf16x8* dst) {
-      r = min(r, total_k - 1);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) dst[st] = *(const bf16x8*)(kr + r * D + st * 16);
+      for (int st = 0; st < 8; ++st)
+        dst[st] = *(const bf16x8*)(kr + min(r + 4 * st, total_k - 1) * D);
     };
-    const int64_t r0 = f + DEC_STEP * wave + (lane & 31);
+    const int64_t r0 = f + DEC_STEP * wave + (lane >> 4);
     pre(r0, b0);
     pre(r0 + DEC_STEP * DEC_WAVES, b1);
     pre(r0 + 2 * DEC_STEP * DEC_WAVES, b2);
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
       const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
       decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg + DEC_STEP * wave, s_end,
                          scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES, decltype(preloaded)::value,
-                         b0, b1, b2);
+                         b0, b1, b2, xbuf[wave]);
     }
     return seg_end;
   };
