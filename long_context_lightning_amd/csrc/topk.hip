@@ -67,7 +67,9 @@ struct TopkShared {
   uint32_t red_c[TK_WAVES];            // wave exchanges of the compaction
   uint32_t red_d[TK_WAVES];
   uint32_t sel_bin, sel_need, sel_count, sel_min, sel_max;
-  int32_t obuf[TK_OBUF];               // selected positions, written out coalesced at the end
+  // selected positions, written out coalesced at the end; the last WAVE entries take the
+  // writes of lanes whose element is not selected (one per lane, so no store needs a branch)
+  int32_t obuf[TK_OBUF + WAVE];
   float cand_val[TK_OBUF];             // candidates of a streamed row (scores, positions)
   int32_t cand_pos[TK_OBUF];
 };
@@ -135,7 +137,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   // Positions fit in 32 bits (they are stored as int32).
   const int off = (int)((reinterpret_cast<uintptr_t>(srow) >> 2) & 3);
   const f32x4* g4 = reinterpret_cast<const f32x4*>(srow - off);
-  const int lane_g = wave * SLICE4 + lane;       // group of unit 0 in chunk 0
+  // Single-chunk rows (MODE 0) give each lane UNITS consecutive groups, so its elements are
+  // consecutive positions and the compaction is one in-order walk per lane; longer rows keep
+  // the unit-major layout (each load instruction reads 64 consecutive groups).
+  constexpr bool contiguous = MODE == 0;
+  constexpr int USTEP = contiguous ? 1 : WAVE;   // group distance of a lane's units
+  const int lane_g = wave * SLICE4 + lane * (contiguous ? UNITS : 1);   // unit 0, chunk 0
   const float qnan = __uint_as_float(0x7fc00000u);
   // If the row's whole allocated span fits one register chunk, its loads go out before the
   // sequence lookup (the row's address does not depend on it) and the visible length masks
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   if (early) {
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) {
-      const int g = lane_g + u * WAVE;
+      const int g = lane_g + u * USTEP;
       pre[u] = g < ng4_span ? g4[g] : f32x4{qnan, qnan, qnan, qnan};
     }
   }
@@ -162,12 +169,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   const int nchunks = (ng4 + CHUNK4 - 1) / CHUNK4;
 
   float x[UNITS][4];
-  // Unit u of this lane in chunk c is group c*CHUNK4 + lane_g + 64*u; its element e is
+  // Unit u of this lane in chunk c is group c*CHUNK4 + lane_g + USTEP*u; its element e is
   // position 4*group + e - off.
   auto load_chunk = [&](int c) {
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) {
-      const int g = c * CHUNK4 + lane_g + u * WAVE;
+      const int g = c * CHUNK4 + lane_g + u * USTEP;
       f32x4 v = {qnan, qnan, qnan, qnan};
       if (g < ng4) v = g4[g];
 #pragma unroll
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     for (int u = 0; u < UNITS; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int pos = 4 * (lane_g + u * WAVE) + e - off;
+        const int pos = 4 * (lane_g + u * USTEP) + e - off;
         x[u][e] = (pos >= 0 && pos < ni) ? pre[u][e] : qnan;
       }
   } else {
@@ -343,7 +350,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 
   // Compaction in index order: a position is taken if its score is above thr, or equal to it
   // and among the first thr_need such positions; the slot of a taken position is the number of
-  // positions taken before it. sink(slot, position, score) stores one taken position.
+  // positions taken before it. sink(take, slot, position, score) stores a position: a taken one
+  // at its slot, any other (the branch-free walk of single-chunk rows) at the lane's spare entry.
   // The candidates of a streamed row come first (all their positions precede the chunk's).
   auto compact_cands = [&](float thr, uint32_t thr_need, uint32_t& gt_tot, uint32_t& eq_tot,
                            auto&& sink) {
@@ -370,10 +378,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       if (cv[j] > thr) {
-        sink(gt_b + min(eq_b, thr_need), cp[j], cv[j]);
+        sink(true, gt_b + min(eq_b, thr_need), cp[j], cv[j]);
         ++gt_b;
       } else if (cv[j] == thr) {
-        if (eq_b < thr_need) sink(gt_b + eq_b, cp[j], cv[j]);
+        if (eq_b < thr_need) sink(true, gt_b + eq_b, cp[j], cv[j]);
         ++eq_b;
       }
     }
@@ -381,76 +389,114 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   // chunk c (x holding it); gt_chunk / eq_chunk count the scores above / equal to thr before it
   auto compact_chunk = [&](int c, float thr, uint32_t thr_need, uint32_t& gt_chunk,
                            uint32_t& eq_chunk, auto&& sink) {
-    uint32_t gt = 0, eq = 0;
+    if constexpr (contiguous) {
+      // Each lane counts its own elements; wave prefix sums and one exchange of wave totals
+      // give the counts before each lane, which then walks its consecutive positions in order
+      // (a taken position's slot is the number of positions taken before it).
+      uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int u = 0; u < UNITS; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gt += (uint32_t)__popcll(__ballot(x[u][e] > thr));
-        eq += (uint32_t)__popcll(__ballot(x[u][e] == thr));
-      }
-    if (lane == 0) { sh.red_c[wave] = gt; sh.red_d[wave] = eq; }
-    __syncthreads();
-    uint32_t gt_before = gt_chunk, eq_before = eq_chunk;
-#pragma unroll
-    for (int w = 0; w < TK_WAVES; ++w) {
-      const uint32_t a = sh.red_c[w], b = sh.red_d[w];
-      if (w < wave) { gt_before += a; eq_before += b; }
-      gt_chunk += a;
-      eq_chunk += b;
-    }
-    __syncthreads();                             // red_c / red_d are reused by the next chunk
-    uint32_t eqc = eq_before;                    // equal scores before the current step
-    uint32_t base = gt_before + min(eq_before, thr_need);  // output slot of the step's first take
-#pragma unroll
-    for (int u = 0; u < UNITS; ++u) {
-      // step u covers positions (lane, e) in lane-major order
-      uint64_t tm[4];
-      uint64_t eq_any = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tm[e] = __ballot(x[u][e] > thr);
-        eq_any |= __ballot(x[u][e] == thr);
-      }
-      if (eq_any) {                              // some scores equal thr: rank them
-        uint64_t qm[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qm[e] = __ballot(x[u][e] == thr);
-        uint32_t rank = eqc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rank += lanes_below(qm[e]);
+      for (int u = 0; u < UNITS; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool is_eq = x[u][e] == thr;
-          tm[e] |= __ballot(is_eq && rank < thr_need);
-          rank += is_eq;
+          gt += x[u][e] > thr;
+          eq += x[u][e] == thr;
+        }
+      const uint32_t igt = wave_incl_scan_u32(gt), ieq = wave_incl_scan_u32(eq);
+      if (lane == WAVE - 1) { sh.red_c[wave] = igt; sh.red_d[wave] = ieq; }
+      __syncthreads();
+      uint32_t gt_b = gt_chunk + igt - gt, eq_b = eq_chunk + ieq - eq;
+#pragma unroll
+      for (int w = 0; w < TK_WAVES; ++w) {
+        const uint32_t a = sh.red_c[w], b = sh.red_d[w];
+        if (w < wave) { gt_b += a; eq_b += b; }
+        gt_chunk += a;
+        eq_chunk += b;
+      }
+      const int p0 = 4 * (c * CHUNK4 + lane_g) - off;
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = x[u][e];
+          const bool above = v > thr, equal = v == thr;
+          const uint32_t slot = gt_b + (above ? min(eq_b, thr_need) : eq_b);
+          sink((above || (equal && eq_b < thr_need)) && slot < (uint32_t)k, slot,
+               p0 + 4 * u + e, v);
+          gt_b += above;
+          eq_b += equal;
+        }
+    } else {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gt += (uint32_t)__popcll(__ballot(x[u][e] > thr));
+          eq += (uint32_t)__popcll(__ballot(x[u][e] == thr));
+        }
+      if (lane == 0) { sh.red_c[wave] = gt; sh.red_d[wave] = eq; }
+      __syncthreads();
+      uint32_t gt_before = gt_chunk, eq_before = eq_chunk;
+#pragma unroll
+      for (int w = 0; w < TK_WAVES; ++w) {
+        const uint32_t a = sh.red_c[w], b = sh.red_d[w];
+        if (w < wave) { gt_before += a; eq_before += b; }
+        gt_chunk += a;
+        eq_chunk += b;
+      }
+      __syncthreads();                             // red_c / red_d are reused by the next chunk
+      uint32_t eqc = eq_before;                    // equal scores before the current step
+      uint32_t base = gt_before + min(eq_before, thr_need);  // output slot of the step's first take
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        // step u covers positions (lane, e) in lane-major order
+        uint64_t tm[4];
+        uint64_t eq_any = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tm[e] = __ballot(x[u][e] > thr);
+          eq_any |= __ballot(x[u][e] == thr);
+        }
+        if (eq_any) {                              // some scores equal thr: rank them
+          uint64_t qm[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qm[e] = __ballot(x[u][e] == thr);
+          uint32_t rank = eqc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rank += lanes_below(qm[e]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool is_eq = x[u][e] == thr;
+            tm[e] |= __ballot(is_eq && rank < thr_need);
+            rank += is_eq;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) eqc += (uint32_t)__popcll(qm[e]);
+        }
+        uint32_t slot = base;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) slot += lanes_below(tm[e]);
+        const int p0 = 4 * (c * CHUNK4 + lane_g + u * USTEP) - off;
+        const uint64_t lane_bit = 1ull << lane;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (tm[e] & lane_bit) {
+            if (slot < (uint32_t)k) sink(true, slot, p0 + e, x[u][e]);
+            ++slot;
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) eqc += (uint32_t)__popcll(qm[e]);
+        for (int e = 0; e < 4; ++e) base += (uint32_t)__popcll(tm[e]);
       }
-      uint32_t slot = base;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) slot += lanes_below(tm[e]);
-      const int p0 = 4 * (c * CHUNK4 + lane_g + u * WAVE) - off;
-      const uint64_t lane_bit = 1ull << lane;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (tm[e] & lane_bit) {
-          if (slot < (uint32_t)k) sink(slot, p0 + e, x[u][e]);
-          ++slot;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) base += (uint32_t)__popcll(tm[e]);
     }
   };
 
   // with k <= TK_OBUF the output is staged in LDS (every slot starts at -1) and written out
   // with coalesced stores at the end
   const bool staged = k <= TK_OBUF;
-  auto out_sink = [&](uint32_t slot, int pos, float) {
-    if (staged) sh.obuf[slot] = pos;
-    else orow[slot] = pos;
+  auto out_sink = [&](bool take, uint32_t slot, int pos, float) {
+    if (staged) sh.obuf[take ? slot : TK_OBUF + lane] = pos;
+    else if (take) orow[slot] = pos;
   };
   if (staged)
     for (int i = tid; i < k; i += TK_THREADS) sh.obuf[i] = -1;
@@ -474,7 +520,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       select(thr, thr_need);
       uint32_t gt_tot = 0, eq_tot = 0;
       if (c + 1 < nchunks) {                     // the segment's top k become the candidates
-        auto cand_sink = [&](uint32_t slot, int pos, float v) {
+        auto cand_sink = [&](bool, uint32_t slot, int pos, float v) {
           sh.cand_val[slot] = v;
           sh.cand_pos[slot] = pos;
         };
