@@ -169,6 +169,54 @@ def test_multi_query_decode_full_size():
     check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
 
 
+def test_graph_capture_replays_match_eager():
+    """The three calls captured in one HIP graph: every replay, with eager work and
+    synchronisations between the replays, reproduces the eager results bit for bit (the calls
+    allocate nothing and record no memset, so a captured step is the eager step)."""
+    case = _small_case("graph_b8_l9000", (9000, 3000, 16384, 2500, 700, 12000, 5000, 2049),
+                       (1,) * 8)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    T, ld = case.total_q, batch.max_seqlen_k
+    scores = torch.zeros((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((T, case.index_topk), dtype=torch.int32, device="cuda")
+    out = torch.zeros((T, case.n_heads, case.d_v), dtype=case.dtype, device="cuda")
+    lse = torch.zeros((T, case.n_heads), dtype=torch.float32, device="cuda")
+    wsn = dsa.workspace_size(dsa.OP_SPARSE_MLA, batch, case.index_topk, case.n_heads, case.d_v)
+    ws = torch.zeros(max(wsn, 1), dtype=torch.uint8, device="cuda")
+    L = dsa.lib()
+
+    def step(stream):
+        sp = stream.cuda_stream
+        st = L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
+                                  d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
+                                  1, scores.data_ptr(), ld, sp)
+        st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
+                         None, 0, sp)
+        st |= L.dsa_sparse_mla_fwd(batch.ptr, d["q"][0].data_ptr(), d["kv"][0].data_ptr(),
+                                   idx.data_ptr(), case.index_topk, case.n_heads, case.d_qk,
+                                   case.d_v, case.softmax_scale, 1, out.data_ptr(),
+                                   lse.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        assert st == 0, st
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (scores, idx, out, lse)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(4):
+        for t in (scores, idx, out, lse):
+            t.zero_()                            # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("scores", "indices", "out", "lse"), (scores, idx, out, lse), ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
+    row_properties(case, idx)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(T))
+
+
 @pytest.mark.slow
 def test_prefill_chunk8k_l64k_sampled():
     case = DI.CASES["prefill_chunk8k_l64k"]
