@@ -17,6 +17,7 @@ duration from K launches back to back between two events, which the rocprofv3 ke
 match), and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--launch", choices=["eager", "graph"], default="eager",
-                    help="headline: steps launched kernel by kernel (default) or replayed from "
+                    help="headline: one dsa_forward call per layer (default) or replayed from "
                          "one HIP graph per input set; the other mode is timed too")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -213,9 +214,30 @@ def main():
     lse = torch.empty((T, case.n_heads), dtype=torch.float32, device="cuda")
     ws_n = dsa.workspace_size(dsa.OP_SPARSE_MLA, batch, case.index_topk, case.n_heads, case.d_v)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    tws_n = dsa.workspace_size(dsa.OP_TOPK, batch, case.index_topk)
+    tws = torch.empty(max(tws_n, 1), dtype=torch.uint8, device="cuda")
+    fws_n = dsa.workspace_size(dsa.OP_FORWARD, batch, case.index_topk, case.n_heads, case.d_v)
+    fws = torch.empty(max(fws_n, 1), dtype=torch.uint8, device="cuda")
     L = dsa.lib()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    # arguments of the fused call, per input set and layer (built once, outside the timing)
+    fargs = [[dsa._CForwardArgs(d["q_idx"].data_ptr(), d["k_idx"].data_ptr(), d["w"].data_ptr(),
+                                case.index_n_heads, case.index_head_dim, case.index_topk,
+                                d["q"][l].data_ptr(), d["kv"][l].data_ptr(), case.n_heads,
+                                case.d_qk, case.d_v, case.softmax_scale, 1)
+              for l in range(case.layers)] for d in sets]
+
+    def fused_on(i, sp):
+        # one dsa_forward per layer: the first runs indexer + top-k into the shared indices,
+        # the other layers of the IndexShare group reuse them
+        st = 0
+        for l in range(case.layers):
+            st |= L.dsa_forward(batch.ptr, ctypes.byref(fargs[i % nsets][l]), idx.data_ptr(),
+                                1 if l == 0 else 0, outs[l].data_ptr(), lse.data_ptr(),
+                                fws.data_ptr(), fws.numel(), sp)
+        if st:
+            raise RuntimeError(f"libdsa call failed with status {st}")
 
     def step(i, ev=None):
         step_on(i, sp, ev)
@@ -230,7 +252,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
-                         None, 0, sp)
+                         tws.data_ptr(), tws.numel(), sp)
         if ev is not None:
             ev[2].record(stream)
         for l in range(case.layers):       # IndexShare: the group's layers reuse the indices
@@ -244,6 +266,7 @@ def main():
             raise RuntimeError(f"libdsa call failed with status {st}")
 
     for i in range(args.warmup):
+        fused_on(i, sp)
         step(i)
     torch.cuda.synchronize()
 
@@ -253,31 +276,35 @@ def main():
         for i in range(nsets):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step_on(i, torch.cuda.current_stream().cuda_stream)
+                fused_on(i, torch.cuda.current_stream().cuda_stream)
             graphs.append(g)
         for i in range(max(2, nsets)):
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
 
-    def time_steps(use_graphs):
+    def time_steps(mode):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            if use_graphs:
+            if mode == "graph":
                 graphs[(args.warmup + i) % nsets].replay()
+            elif mode == "fused":
+                fused_on(args.warmup + i, sp)
             else:
                 step(args.warmup + i)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # timed region 1: the headline, K whole steps, in both launch modes
-    ms_eager = time_steps(False)
-    ms_graph = time_steps(True) if graphs else None
+    # timed region 1: the headline, K whole steps through the fused call (one dsa_forward per
+    # layer), then the same K steps as three separate calls and as graph replays
+    ms_eager = time_steps("fused")
+    ms_separate = time_steps("separate")
+    ms_graph = time_steps("graph") if graphs else None
     ms_step = ms_graph if args.launch == "graph" else ms_eager
     graph_info = None
     if graphs:
         # a replay must reproduce the eager step bit for bit (same kernels, same inputs)
-        step(0)
+        fused_on(0, sp)
         torch.cuda.synchronize()
         ref = [o.clone() for o in outs] + [idx.clone()]
         graphs[0].replay()
@@ -373,6 +400,7 @@ def main():
                    "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets,
                    "launch": "hip_graph" if args.launch == "graph" else "eager"},
         "eager_ms_per_step": round(ms_eager, 5),
+        "separate_calls_ms_per_step": round(ms_separate, 5),
         "graph": graph_info,
         "achieved_hbm_gbps": round(sb / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": sb,
