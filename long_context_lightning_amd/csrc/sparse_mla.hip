@@ -49,15 +49,15 @@ constexpr int ROWB = DQK * 2;                // 1152 bytes per latent row
 constexpr int CHUNKS = ROWB / 16;            // 72 chunks of 16 B
 constexpr int STAGE_BYTES = TILE * ROWB;     // 73728
 constexpr int ROPE_OFF = DV * 2;             // byte offset of the RoPE columns in a row
-constexpr int P_STRIDE = TILE + 8;           // bf16 elements per head row of P (padded)
-constexpr int R_BYTES = NWAVES * 8 * 64 * 4; // QK exchange (8 floats per lane per wave), then P
+constexpr int XSLOT = 8 * 64 * 4;            // exchange slot of one wave: 8 floats per lane
+constexpr int R_BYTES = NWAVES * XSLOT;      // QK exchange, then each wave's P (see below)
 constexpr int MLA_LDS = 2 * STAGE_BYTES + R_BYTES;   // 160 KB: one workgroup per CU
 constexpr int LOADS_PER_THREAD = STAGE_BYTES / 16 / NTHREADS;   // 9
 constexpr int QK_STEPS = DQK / 16 / 2;       // 18 MFMA k-steps per K half
 constexpr int VB_WAVE = DV / 32 / 4;         // 4 value blocks of 32 columns per wave
 static_assert(LOADS_PER_THREAD * NTHREADS * 16 == STAGE_BYTES, "stage must split evenly");
 static_assert(LOADS_PER_THREAD % 3 == 0, "gathers are issued in groups of three");
-static_assert(WG_HEADS * P_STRIDE * 2 <= R_BYTES, "P fits the exchange region");
+static_assert(HG * 32 * 2 <= XSLOT, "a wave's P (32 heads x 32 rows) fits one exchange slot");
 static_assert(WG_HEADS * DV * 2 <= STAGE_BYTES, "the output block fits one stage");
 static_assert(MLA_LDS <= 160 * 1024, "LDS of one CU");
 
@@ -186,8 +186,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
   const int ntiles = (qp.p >= 0 && L > 0 && r_end > r_beg) ? (r_end - r_beg + TILE - 1) / TILE : 0;
   const __bf16* kvb = kv + qp.key_base * DQK;
+  // QK exchange: wave w writes slot w and reads slot w^1, which no other wave reads. Once its
+  // reads have returned, wave w reuses slot w^1 for its probabilities: [2][32 heads][8 rows]
+  // bf16 (row group g of its 16 rows per head; lane half h holds rows 4h..4h+3 of a group), so
+  // no wave writes a slot that another wave may still be reading.
   float* xch = (float*)rbuf;                  // [8 waves][2][64 lanes][4]
-  __bf16* pl = (__bf16*)rbuf;                 // [64 heads][P_STRIDE], after the exchange is read
 
   // Softmax with a fixed reference maximum per head: the first tile in which a head has a finite
   // logit sets its reference m_ref, and probabilities are exp2(s - m_ref) without rescaling the
@@ -365,8 +368,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
           ls += p;
           pk[e] = (__bf16)p;
         }
-        const int row0 = 32 * rb + 16 * g + 8 * kh + 4 * half;
-        *(bf16x4*)(pl + (hl * HG + c32) * P_STRIDE + row0) = pk;
+        // rows 32*rb + 16*g + 8*kh + 4*half + e of head c32
+        *(bf16x4*)(rbuf + (wave ^ 1) * XSLOT + (g * HG + c32) * 16 + half * 8) = pk;
       }
       ls = halves_sum(ls);
       if (half == 0) *stat(stage, ST_SUM + wave * HG + c32) = ls;
@@ -488,10 +491,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
           vb[rr][0] = pp + 64 * b2;    // even blk: blk ^ b2 = blk + b2
           vb[rr][1] = pp - 64 * b2;    // odd blk:  blk ^ b2 = blk - b2
         }
-        const __bf16* pbase = pl + (hl * HG + c32) * P_STRIDE + half * 8;
+        // P rows 16*ks + 8*half .. +7 of head c32 were written by wave (hl, rb = ks/2, kh = half)
+        // into slot 4*hl + 2*(ks/2) + (half^1), row group ks%2
+        const char* pbase = rbuf + (4 * hl + (half ^ 1)) * XSLOT + c32 * 16;
 #pragma unroll
         for (int ks = 0; ks < TILE / 16; ++ks) {
-          const bf16x8 pa = *(const bf16x8*)(pbase + ks * 16);
+          const bf16x8 pa = *(const bf16x8*)(pbase + (ks >> 1) * 2 * XSLOT + (ks & 1) * HG * 16);
 #pragma unroll
           for (int db = 0; db < VB_WAVE; ++db) {
             const int blk = VB_WAVE * cq + db;
