@@ -67,6 +67,10 @@ struct TopkShared {
   uint32_t red_c[TK_WAVES];            // wave exchanges of the compaction
   uint32_t red_d[TK_WAVES];
   uint32_t sel_bin, sel_need, sel_count, sel_min, sel_max;
+  // scores of a round-0 bin with at most WAVE entries (NaN past the count), ranked by one wave
+  __attribute__((aligned(16))) float few[WAVE];
+  uint32_t few_n, few_need;
+  float few_thr;
   // selected positions, written out coalesced at the end; the last WAVE entries take the
   // writes of lanes whose element is not selected (one per lane, so no store needs a branch)
   int32_t obuf[TK_OBUF + WAVE];
@@ -247,6 +251,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       sh.bmax[0][i] = 0u;
       sh.bmax[1][i] = 0u;
     }
+    if (tid < WAVE) sh.few[tid] = qnan;
+    if (tid == 0) sh.few_n = 0;
     // value range (fminf / fmaxf skip NaN)
     float xmin = __int_as_float(0x7f800000), xmax = -xmin;
     visit([&](float v) {
@@ -279,6 +285,35 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       select_bin(sh.hist[0], sh.bmin[0], sh.bmax[0], need, sh);
       const uint32_t bin0 = sh.sel_bin;
       need = sh.sel_need;
+      if (sh.sel_count <= (uint32_t)WAVE) {
+        // Few scores in bin0: they go to LDS and one wave ranks them. The need-th largest is
+        // the threshold; of the scores equal to it, those not counted above it are taken.
+        visit([&](float v) {
+          if (lin_bin(v, s0, c0) == bin0) sh.few[atomicAdd(&sh.few_n, 1u)] = v;
+        });
+        __syncthreads();
+        if (wave == 0) {
+          const float v = sh.few[lane];
+          uint32_t gt = 0, eq = 0;
+#pragma unroll
+          for (int j = 0; j < WAVE / 4; ++j) {
+            const f32x4 u = reinterpret_cast<const f32x4*>(sh.few)[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              gt += u[e] > v ? 1u : 0u;
+              eq += u[e] == v ? 1u : 0u;
+            }
+          }
+          if (gt < need && need <= gt + eq) {    // NaN entries have eq = 0
+            sh.few_thr = v;
+            sh.few_need = need - gt;
+          }
+        }
+        __syncthreads();
+        thr = sh.few_thr;
+        thr_need = sh.few_need;
+        return;
+      }
       // round 1: the scores of bin0, in 2048 linear sub-bins with their smallest and largest key
       float s1 = s0 * (float)TK_BINS;
       float c1 = -(xmin + (float)bin0 / s0) * s1;
@@ -491,9 +526,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     }
   };
 
-  // with k <= TK_OBUF the output is staged in LDS (every slot starts at -1) and written out
-  // with coalesced stores at the end
-  const bool staged = k <= TK_OBUF;
+  // Streamed rows with k <= TK_OBUF stage the output in LDS (every slot starts at -1) and
+  // write it out with coalesced stores at the end. Single-chunk rows store each selected
+  // position straight to memory: a lane's positions go to consecutive slots, and with n > k
+  // exactly k are selected, so every slot is written.
+  const bool staged = MODE != 0 && k <= TK_OBUF;
   auto out_sink = [&](bool take, uint32_t slot, int pos, float) {
     if (staged) sh.obuf[take ? slot : TK_OBUF + lane] = pos;
     else if (take) orow[slot] = pos;
