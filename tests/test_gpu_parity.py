@@ -484,6 +484,26 @@ def test_topk_crafted_rows():
     _crafted_topk([r[:5000] for r in rows], 7)
 
 
+def _few_bin_row(rng, n_bin):
+    """A row whose k-th largest score (k = 2048) lies in a linear round-0 bin holding n_bin
+    scores with ties: the range [0, 2048] gives bins of width 1, 2000 distinct scores sit in
+    bins 1000..1999, the bin [500, 501) holds n_bin scores in three tie groups, and 6000
+    scores lie below it, in shuffled positions."""
+    hi = 1000.0 + 0.5 * np.arange(2000)
+    groups = [500.75] * 34 + [500.5] * 20 + [500.25] * 10 + [500.125] * (n_bin - 64)
+    lo = rng.random(6000) * 499.0
+    row = np.concatenate([hi, groups, lo, [0.0, 2048.0]]).astype(np.float32)
+    return row[rng.permutation(row.shape[0])]
+
+
+def test_topk_few_scores_in_the_threshold_bin():
+    """64 scores in the threshold's round-0 bin are ranked directly; 65 take the second
+    histogram round. Both must match the oracle, ties going to the lowest positions."""
+    rng = np.random.default_rng(21)
+    rows = [_few_bin_row(rng, 64), _few_bin_row(rng, 65), _few_bin_row(rng, 64)[:5000]]
+    _crafted_topk(rows, 2048)
+
+
 def test_topk_many_long_rows():
     """More rows than the split-row path takes: one workgroup per row, the row in chunks."""
     rng = np.random.default_rng(9)
