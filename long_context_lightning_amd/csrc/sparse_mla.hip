@@ -7,14 +7,16 @@
 // workgroup per CU. Waves 0-3 serve heads 0-31 of the group and waves 4-7 heads 32-63; both
 // halves compute on the same gathered tile.
 //   * Tiles of 64 selected rows are gathered straight from HBM into LDS with direct
-//     global->LDS 16-byte loads, double-buffered: the gathers of tile i+1 are in flight while
-//     tile i computes, and those of tile i+2 go out as soon as tile i's stage is consumed. The
-//     top of a tile waits until only the next tile's nine gathers per lane are outstanding, so
-//     the prefetch is never drained there. Each row's 72 chunks of 16 B are stored with the
+//     global->LDS 16-byte loads, double-buffered: the gathers of tile i+1 go out during tile
+//     i's QK^T (once the barrier that ended tile i-1 has freed their stage) and land while
+//     tile i computes; at the end of tile i each wave waits for its own gathers and one barrier
+//     publishes tile i+1 to the workgroup. Each row's 72 chunks of 16 B are stored with the
 //     chunk slot XOR-ed by a 3-bit function of the row (swz) that keeps every MFMA operand read
 //     free of LDS bank conflicts.
-//   * The first indices and the query block are loaded before the sequence lookup, so the two
-//     latencies overlap at the start of the workgroup.
+//   * The first two tiles' indices are loaded before the sequence lookup, so the two latencies
+//     overlap at the start of the workgroup; the query block is gathered right behind the
+//     first tile. (Gathering it before the lookup was measured: the lookup's memory wait then
+//     drains it first and the first tile goes out later, for no gain.)
 //   * QK^T is computed transposed, S^T[rows x heads] = KV[rows x 576] * Q^T, on 32x32x16 MFMAs:
 //     in each head half, wave (rb, kh) owns rows 32*rb.. and K half kh for all 32 heads; the
 //     query half is resident in registers (B operand). The two K-half partial sums of a row
