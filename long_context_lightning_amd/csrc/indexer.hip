@@ -10,9 +10,10 @@
 //
 //  * decode kernel: few queries per sequence. A workgroup owns 1024 consecutive rows of the
 //    flattened key cache; its 4 waves take every fourth 32-key step of each sequence segment in
-//    it, so the workgroup reads one contiguous stream. Key rows go straight from HBM into
-//    registers (B operand), two steps ahead, with the query's heads resident (A operand). Work is
-//    laid over the flattened key rows, so ragged batches need no padding.
+//    it, so the workgroup reads one contiguous stream. Key rows are loaded coalesced (each load
+//    instruction reads four whole rows) into registers two steps ahead and pass through an 8 KB
+//    LDS region per wave into the B-operand layout, with the query's heads resident (A
+//    operand). Work is laid over the flattened key rows, so ragged batches need no padding.
 //  * prefill kernel: many queries per sequence (chunked prefill). A workgroup of 8 waves owns 16
 //    queries (2 per wave, A operands in registers) and walks the causal key range in 64-key
 //    tiles staged in LDS by direct global->LDS loads through a 4-stage ring (three tiles load

@@ -23,7 +23,8 @@
 //     block are exchanged through LDS, each wave keeping half of the block's elements, so
 //     every lane holds one head.
 //   * Softmax in fp32 (base-2 exponent, scale*log2(e) folded into the logits) against a fixed
-//     reference maximum per head; P is rounded to bf16 into LDS.
+//     reference maximum per head, raised (with the output block rescaled) only when a logit
+//     exceeds it by more than 2^16; P is rounded to bf16 into LDS.
 //   * P*V on 32x32x16 MFMAs: wave w of a head half owns value columns 128*w.. of its 32 heads;
 //     P is the A operand, V (row-major in the same LDS tile) is read column-wise with the
 //     gfx950 transposing LDS read. The fp32 output block stays in registers across tiles.
@@ -31,7 +32,8 @@
 //     in the accumulator register layout (32 contiguous bytes per lane and value block), and
 //     its log-sum-exp; a combine kernel merges them with exp(lse_i - lse) weights. With one
 //     split the output block is transposed through LDS and written with 16-byte stores.
-//   * Splits: about one workgroup per CU in total (256), down to one tile per split.
+//   * Splits: about one workgroup per CU in total (256), but at least two tiles per split (a
+//     split's first tile waits out the whole gather latency; its second overlaps it).
 #include <algorithm>
 
 #include "common.hpp"

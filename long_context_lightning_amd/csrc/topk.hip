@@ -8,13 +8,17 @@
 // Batches of many rows (prefill, wide decode) use one workgroup of 1024 threads per query row,
 // described here; batches of a few long rows split each row over several workgroups (further
 // down). With one workgroup per row the scores stay in registers:
-//   * the row is cut into chunks of UNITS*4096 positions (UNITS <= 8); inside a chunk, wave w
-//     owns a contiguous slice and lane l of it holds UNITS 16-byte groups, (u*64 + l) within it.
-//     A row of at most one chunk is read from memory once; longer rows re-read their chunks on
-//     every pass. Slots outside the row hold NaN, which no comparison or bin counts;
+//   * the row is cut into chunks of UNITS*4096 positions (UNITS <= 8) held in registers. A row
+//     of one chunk gives each lane UNITS consecutive 16-byte groups (consecutive positions);
+//     longer rows keep a unit-major layout, lane l of wave w's slice holding groups u*64 + l.
+//     A row of one chunk is read from memory once. A longer row is streamed once when k fits
+//     the candidate buffer (after each chunk only the top k of candidates and chunk survive,
+//     in LDS); otherwise its chunks are re-read on every pass. Slots outside the row hold NaN,
+//     which no comparison or bin counts;
 //   * round 0 histograms every score into 2048 bins linear in the value between the row's
-//     smallest and largest score; round 1 splits the bin holding the k-th largest score into
-//     2048 finer linear bins; later rounds split the chosen bin in the space of order-preserving
+//     smallest and largest score. If the bin holding the k-th largest score has at most 64
+//     scores, one wave ranks them directly. Otherwise round 1 splits that bin into 2048 finer
+//     linear bins, and later rounds split the chosen bin in the space of order-preserving
 //     32-bit keys into bins of a power-of-two width (at most three such rounds reach one key).
 //     Bin indices are monotone functions of the score (a rounded fused multiply-add, clamped
 //     and truncated), so every bin is a contiguous range of scores. From round 1 on each bin
@@ -24,10 +28,11 @@
 //     smallest score is taken) or when the bin holds a single value. The result is a threshold
 //     score T and a count `need`: a position is selected if its score is above T, or equal to T
 //     and among the first `need` such positions;
-//   * compaction in index order: per chunk, the per-wave counts (ballot popcounts) are
-//     exchanged once, which gives each wave its first output slot and the number of scores
-//     equal to T before its slice; inside the wave, each step of 256 positions ranks its taken
-//     positions with lane-mask counts.
+//   * compaction in index order: for a row of one chunk each lane counts its scores above and
+//     equal to T, wave prefix sums and one exchange of wave totals give the counts before it,
+//     and the lane stores its taken positions straight to their output slots; for longer rows
+//     the per-wave counts (ballot popcounts) are exchanged once per chunk, and inside the wave
+//     each step of 256 positions ranks its taken positions with lane-mask counts.
 #include <algorithm>
 
 #include "common.hpp"
