@@ -110,7 +110,11 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  *   out     [T, n_heads, d_v]    dtype;  lse [T, n_heads] fp32 or NULL.
  * A query with no valid index gets out = 0 and lse = -inf. Softmax statistics and the output
  * accumulator are fp32; probabilities are rounded to bf16 for the value product on the bf16
- * path. */
+ * path.
+ *   workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes (may be NULL when that is 0).
+ *     When a query's selected rows are split over several workgroups (few queries, bf16), it
+ *     holds each split's normalised partial output (bf16) and log-sum-exp, merged by a second
+ *     kernel. Its contents on entry do not matter; on return they are undefined. */
 dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void* kv,
                               const int32_t* indices, int32_t index_topk, int32_t n_heads,
                               int32_t d_qk, int32_t d_v, float softmax_scale, dsa_dtype dtype,
