@@ -184,8 +184,9 @@ def cpu_baseline(case, sets, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the DSA path on one GPU only; --gpus {args.gpus} is "
-              "not supported (decode shards by sequence, see the design notes)", file=sys.stderr)
+        print(f"bench.py: libdsa runs the DSA path on one GPU; --gpus {args.gpus} is not "
+              "supported (sharding decode by sequence over several GPUs is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import dsa_inputs as DI

@@ -1,0 +1,49 @@
+"""Host-side checks of bench.py (no GPU): its algorithmic byte and FLOP counts against the
+per-step figures worked out independently from the workload shapes, and its refusal of more
+than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import dsa_inputs as DI  # noqa: E402
+
+
+# Decode, 32 x 16384: k_I 32*16384*256 + rows 32*2048*1152 + q/out 32*64*(576+512)*2
+# + q_I/w 32*32*(256+4). IndexShare: one k_I stream and four layers of rows, q and out.
+# Mixed lengths: the k_I rows of every sequence, min(2048, L) rows each, q/out/q_I/w per query.
+@pytest.mark.parametrize("name,step,mla", [
+    ("decode_b32_l16k", 214_437_888, 79_953_920),
+    ("indexshare_b8_l256k", 616_891_392, 19_988_480),
+    ("mixed_b16_l512_1m", 949_534_848, 33_706_624),
+])
+def test_step_bytes(name, step, mla):
+    case = DI.CASES[name]
+    assert bench.step_bytes(case) == step
+    assert bench.mla_bytes(case) == mla
+
+
+def test_decode_bytes_closed_form():
+    b, L, k = 32, 16384, 2048
+    want = b * L * 128 * 2 + b * k * 576 * 2 + b * 64 * (576 + 512) * 2 + b * 32 * (128 * 2 + 4)
+    assert bench.step_bytes(DI.CASES["decode_b32_l16k"]) == want
+
+
+def test_prefill_flops():
+    case = DI.CASES["prefill_chunk8k_l64k"]
+    # queries at positions 57344..65535 each see p + 1 keys: sum = 8192*57344 + 8192*8193/2
+    pairs = 8192 * 57344 + 8192 * 8193 // 2
+    assert bench.indexer_flops(case) == 2 * 32 * 128 * pairs == 4_123_202_158_592
+    assert bench.mla_flops(case) == 2 * 64 * (576 + 512) * 2048 * 8192 == 2_336_462_209_024
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
