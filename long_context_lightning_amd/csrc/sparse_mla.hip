@@ -593,10 +593,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
 // accumulator layout. out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i
 // (natural-log units). Four waves share the splits (wave q takes splits q, q+4, ..); each lane
 // issues all loads of a pass before the weights are known, and the four partial sums meet in
-// LDS.
+// LDS. SPW splits per wave and pass (chosen from the split count, so a pass rarely loads a
+// split twice): every load of a pass is issued unconditionally (the split index clamped), so
+// the compiler counts them and waits for the log-sum-exps alone, which are loaded first.
 constexpr int CMB_THREADS = 256;
-constexpr int CMB_SPW = 8;                     // splits per wave and pass
 
+template <int SPW>
 __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            int nsplit, int H,
@@ -619,20 +621,24 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
   const int64_t stride = (int64_t)nhg32 * 4 * VB_WAVE * 1024;     // elements per (t, split)
   const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((g32 * 4 + w) * VB_WAVE + db) * 1024 +
                      lane * 16;
-  bf16x8 lo8[CMB_SPW], hi8[CMB_SPW];
+  bf16x8 lo8[SPW], hi8[SPW];
   auto load = [&](int base) {
 #pragma unroll
-    for (int j = 0; j < CMB_SPW; ++j) {
-      const int i = base + wv + 4 * j;
-      if (i < nsplit) {
-        lo8[j] = *(const bf16x8*)(po + i * stride);
-        hi8[j] = *(const bf16x8*)(po + i * stride + 8);
-      }
+    for (int j = 0; j < SPW; ++j) {
+      const int i = min(base + wv + 4 * j, nsplit - 1);   // a clamped copy is loaded, not used
+      lo8[j] = *(const bf16x8*)(po + i * stride);
+      hi8[j] = *(const bf16x8*)(po + i * stride + 8);
     }
   };
+  // every split's log-sum-exp of the group's 32 heads. The first one per thread is loaded
+  // before the partial outputs and stored after them: loads complete in issue order, so the
+  // merge weights are computed while the partials are still streaming in.
+  const int nl = nsplit * 32;
+  const float lse_first = tid < nl ? part_lse[((int64_t)t * nsplit + (tid >> 5)) * H + h0 + (tid & 31)]
+                                   : 0.f;
   load(0);
-  // every split's log-sum-exp of the group's 32 heads
-  for (int j = tid; j < nsplit * 32; j += CMB_THREADS)
+  if (tid < nl) wgt[tid] = lse_first;
+  for (int j = tid + CMB_THREADS; j < nl; j += CMB_THREADS)
     wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
   __syncthreads();
   // merge weights exp(lse_i - lse): eight threads per head, each over every eighth split, the
@@ -670,7 +676,7 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   for (int base = 0;;) {
 #pragma unroll
-    for (int j = 0; j < CMB_SPW; ++j) {
+    for (int j = 0; j < SPW; ++j) {
       const int i = base + wv + 4 * j;
       if (i < nsplit) {
 #pragma unroll
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restr
         }
       }
     }
-    base += 4 * CMB_SPW;
+    base += 4 * SPW;
     if (base >= nsplit) break;
     load(base);
   }
@@ -803,9 +809,17 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
       part_o, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  mla_combine<<<dim3(b.total_q, (n_heads / HG) * 4 * VB_WAVE), CMB_THREADS,
-                plan.nsplit * 32 * sizeof(float), stream>>>(part_o, part_lse, plan.nsplit, n_heads,
-                                                            (__bf16*)out, lse);
+  const dim3 cgrid(b.total_q, (n_heads / HG) * 4 * VB_WAVE);
+  const size_t csmem = plan.nsplit * 32 * sizeof(float);
+  if (plan.nsplit <= 8)
+    mla_combine<2><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
+                                                          (__bf16*)out, lse);
+  else if (plan.nsplit <= 16)
+    mla_combine<4><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
+                                                          (__bf16*)out, lse);
+  else
+    mla_combine<8><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
+                                                          (__bf16*)out, lse);
   return hipGetLastError();
 }
 

@@ -286,6 +286,8 @@ def _small_case(name, seqlens_k, seqlens_q, **kw):
     ((37, 3000, 5, 9000, 65), (1, 2, 1, 3, 4), 64),   # ragged decode + multi-query rows
     ((300, 129), (40, 17), 64),              # short prefill chunks (prefill indexer kernel)
     ((4100,), (4100,), 2048),                # whole-sequence prefill
+    ((9000,), (1,), 4096),                   # one query, 32 splits of two tiles each
+    ((5000, 7000), (1, 1), 3000),            # k not a multiple of the 64-row tile, 24 splits
 ])
 def test_ragged_edge_cases(lens, nq, k):
     case = _small_case(f"edge_{lens}_{nq}_{k}", lens, nq, index_topk=k)
