@@ -46,6 +46,7 @@ constexpr int DEC_WAVES = 4;
 constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
 
 constexpr int DEC_STEP = 32;            // keys per MFMA step
+constexpr int DEC_NSTEP = DEC_KEYS_PER_WAVE / DEC_STEP;   // steps of one wave in a workgroup (8)
 
 // Streams key rows s_beg, s_beg + stride, .. (32-key steps) of one sequence for query t, below
 // s_end. Each step's 32 key rows (8 KB) are loaded into registers two steps ahead of the MFMAs,
@@ -62,6 +63,17 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
                                                bool preloaded, bf16x8 (&b0)[8], bf16x8 (&b1)[8],
                                                bf16x8 (&b2)[8], bf16x8* __restrict__ xw) {
   constexpr int HI = 32 * HB;
+  // The range is wave-uniform; stating it (scalar registers) keeps the step loop on scalar
+  // branches, so the compiler's memory-counter waits stay exact: each step waits for its own
+  // rows only, with the next two steps' rows still in flight.
+  auto uni = [](int64_t x) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)x));
+  };
+  s_beg = uni(s_beg);
+  s_end = uni(s_end);
+  kb0 = uni(kb0);
+  t = __builtin_amdgcn_readfirstlane(t);
   const int lane = lane_id();
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -119,15 +131,17 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
     load(min(s_beg + stride, s_end - 1), b1);
     load(min(s_beg + 2 * stride, s_end - 1), b2);
   }
-  for (int64_t s0 = s_beg; s0 < s_end; s0 += 3 * stride) {
-    step(s0, b0);
-    if (s0 + stride >= s_end) break;
-    load(min(s0 + 3 * stride, s_end - 1), b0);
-    step(s0 + stride, b1);
-    if (s0 + 2 * stride >= s_end) break;
-    load(min(s0 + 4 * stride, s_end - 1), b1);
-    step(s0 + 2 * stride, b2);
-    load(min(s0 + 5 * stride, s_end - 1), b2);
+  // A wave has at most DEC_NSTEP steps in one segment (its share of the workgroup's rows), so the
+  // step sequence is unrolled: straight-line code lets the compiler count the loads in flight
+  // exactly, and each step waits for its own rows only (as a loop, the merge of its entry and
+  // back-edge states made the top of every third step wait for nearly every load in flight).
+#pragma unroll
+  for (int i = 0; i < DEC_NSTEP; ++i) {
+    const int64_t s0 = s_beg + (int64_t)i * stride;
+    if (s0 >= s_end) break;                      // uniform
+    bf16x8* cur = i % 3 == 0 ? b0 : (i % 3 == 1 ? b1 : b2);
+    step(s0, cur);
+    if (i + 3 < DEC_NSTEP) load(min(s0 + 3 * stride, s_end - 1), cur);
   }
 }
 
@@ -139,7 +153,9 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
     float* __restrict__ scores, int64_t ld) {
   __shared__ bf16x8 xbuf[DEC_WAVES][DEC_STEP * 16];   // one step of key rows per wave
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar register): the key range and the step loop below are then uniform,
+  // so the loop runs on scalar branches and the compiler's memory-counter waits stay exact
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int j = blockIdx.y;
   int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
