@@ -160,8 +160,14 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   const int j = blockIdx.y;
   int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
   const int64_t f_end = min(f + DEC_KEYS_PER_BLOCK, total_k);
-  // The first three steps' key rows of this wave, by flattened row: their addresses do not
-  // depend on the sequence lookup, so they load while it runs.
+  // The sequence lookup's first loads go out first (lane i: both boundaries of sequence i), then
+  // the first three steps' key rows of this wave by flattened row (their addresses do not depend
+  // on the lookup). Loads complete in issue order, so the lookup resolves without waiting for
+  // the rows, and the query operands it selects are requested while the rows stream in.
+  const int i_first = min(lane, max(nseq - 1, 0));
+  int64_t ka_first = cu_k[i_first], kz_first = cu_k[i_first + 1];
+  int32_t qa_first = cu_q[i_first], qz_first = cu_q[i_first + 1];
+  __builtin_amdgcn_sched_barrier(0);           // keep them ahead of the rows
   bf16x8 b0[8], b1[8], b2[8];
   {
     const __bf16* kr = k_idx + (lane & 15) * 8;
@@ -183,9 +189,20 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     int64_t kb0 = 0, kb1 = 0;
     int q0 = 0, q1 = 0;
     for (int base = 0;; base += WAVE) {
-      const int i = min(base + lane, max(nseq - 1, 0));
-      int64_t ka = cu_k[i], kz = cu_k[i + 1];
-      int32_t qa = cu_q[i], qz = cu_q[i + 1];
+      int64_t ka, kz;
+      int32_t qa, qz;
+      if (decltype(preloaded)::value && base == 0) {   // loaded at the top of the kernel
+        ka = ka_first;
+        kz = kz_first;
+        qa = qa_first;
+        qz = qz_first;
+      } else {
+        const int i = min(base + lane, max(nseq - 1, 0));
+        ka = cu_k[i];
+        kz = cu_k[i + 1];
+        qa = cu_q[i];
+        qz = cu_q[i + 1];
+      }
       asm volatile("" : "+v"(ka), "+v"(kz), "+v"(qa), "+v"(qz));
       const bool le = base + lane + 1 < nseq && kz <= f;
       const int cnt = __popcll(__ballot(le));
