@@ -447,10 +447,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
 #pragma unroll
       for (int qi = 0; qi < 8; ++qi) {
         const float mine = kh ? e1[qi] : e0[qi];
-        const float v = (mine + part[qi >> 2][qi & 3]) * scale_log2;
-        sv[qi] = ((vbits >> (16 * (qi >> 2) + (qi & 3))) & 1) ? v : -INFINITY;
-        mx = fmaxf(mx, sv[qi]);
+        sv[qi] = (mine + part[qi >> 2][qi & 3]) * scale_log2;
       }
+      if (__builtin_expect(vmask != ~0ull, 0)) {   // uniform: some row of the tile is invalid
+#pragma unroll
+        for (int qi = 0; qi < 8; ++qi)
+          sv[qi] = ((vbits >> (16 * (qi >> 2) + (qi & 3))) & 1) ? sv[qi] : -INFINITY;
+      }
+#pragma unroll
+      for (int qi = 0; qi < 8; ++qi) mx = fmaxf(mx, sv[qi]);
       mx = halves_max(mx);                     // this wave's 16 rows, head c32 of its half
       // The tile maxima are exchanged only while some reference is unset; afterwards a logit
       // beyond its reference's headroom is detected from the wave's own rows and flagged with
