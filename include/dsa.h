@@ -108,6 +108,7 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  *   indices [T, index_topk]      int32 sequence-local positions in any order; entries < 0 are
  *                                skipped; entries >= L_b are skipped; duplicates count twice.
  *   out     [T, n_heads, d_v]    dtype;  lse [T, n_heads] fp32 or NULL.
+ * softmax_scale must be finite (DSA_ERR_INVALID_ARG otherwise).
  * A query with no valid index gets out = 0 and lse = -inf. Softmax statistics and the output
  * accumulator are fp32; probabilities are rounded to bf16 for the value product on the bf16
  * path.

@@ -1,5 +1,6 @@
 // C ABI of libdsa: host-side validation, workspace layout and launch sequencing.
 // Every check runs before anything is enqueued; calls only enqueue work on the caller's stream.
+#include <cmath>
 #include <vector>
 
 #include "../../include/dsa.h"
@@ -55,7 +56,7 @@ dsa_status check_mla(const dsa_batch* b, const void* q, const void* kv, const in
                      int32_t k, int32_t h, int32_t dqk, int32_t dv, float scale, dsa_dtype dt,
                      const void* out) {
   if (!batch_ok(b) || !q || !kv || !indices || !out || k <= 0 || h <= 0 || dqk <= 0 ||
-      dv <= 0 || dv > dqk || !(scale == scale))
+      dv <= 0 || dv > dqk || !std::isfinite(scale))
     return DSA_ERR_INVALID_ARG;
   if (dt == DSA_BF16) {
     if (dqk != 576 || dv != 512 || h % 32 != 0) return DSA_ERR_UNSUPPORTED;

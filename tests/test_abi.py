@@ -98,8 +98,9 @@ def test_sparse_mla_rejects_bad_arguments(L):
     assert f(*a) == UNSUPPORTED
     a = list(args); a[6] = 512; a[7] = 448   # other latent widths are not compiled
     assert f(*a) == UNSUPPORTED
-    a = list(args); a[8] = float("nan")
-    assert f(*a) == INVALID
+    for bad in (float("nan"), float("inf"), float("-inf")):   # softmax scale must be finite
+        a = list(args); a[8] = bad
+        assert f(*a) == INVALID
     a = list(args); a[9] = 0; a[4] = 100000  # fp32 path keeps one softmax row in LDS
     assert f(*a) == UNSUPPORTED
     # 2 decode queries over 64 heads split the selection: a workspace is required
