@@ -156,6 +156,37 @@ def test_decode_forward_matches_separate_calls():
     assert torch.equal(i1, i3) and torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def test_forward_reuse_with_the_attention_workspace_only():
+    """compute_indices = 0 reads the cached indices and needs only the sparse-MLA part of the
+    forward workspace (placed at its start): a workspace of exactly that size, through the C
+    ABI, gives the separate sparse-MLA call's output bit for bit."""
+    import ctypes
+    case = DI.CASES["decode_b32_l16k"]
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    _, idx, o1, l1 = run_path(case, d, batch)
+    L = dsa.lib()
+    T, H = case.total_q, case.n_heads
+    n_mla = dsa.workspace_size(dsa.OP_SPARSE_MLA, batch, case.index_topk, H, case.d_v)
+    assert 0 < n_mla < dsa.workspace_size(dsa.OP_FORWARD, batch, case.index_topk, H, case.d_v)
+    ws = torch.empty(n_mla, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H, case.d_v), dtype=case.dtype, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    args = dsa._CForwardArgs(None, None, None, case.index_n_heads, case.index_head_dim,
+                             case.index_topk, d["q"][0].data_ptr(), d["kv"][0].data_ptr(), H,
+                             case.d_qk, case.d_v, case.softmax_scale, 1)
+    sp = torch.cuda.current_stream().cuda_stream
+    st = L.dsa_forward(batch.ptr, ctypes.byref(args), idx.data_ptr(), 0, out.data_ptr(),
+                       lse.data_ptr(), ws.data_ptr(), n_mla, sp)
+    assert st == 0, st
+    # one byte short is refused before anything is launched
+    st = L.dsa_forward(batch.ptr, ctypes.byref(args), idx.data_ptr(), 0, out.data_ptr(),
+                       lse.data_ptr(), ws.data_ptr(), n_mla - 1, sp)
+    assert st == 3, st
+    torch.cuda.synchronize()
+    assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
 def test_multi_query_decode_full_size():
     """Two to four new query tokens per sequence (speculative / multi-token decode) at the
     decode sizes: 16 sequences of 16384 tokens, top-2048, 64 heads; every row checked."""
