@@ -130,9 +130,11 @@ def traffic_record(workload, kernel):
 
 
 def cpu_baseline(case, sets, budget_s):
-    """The oracle as it stands, on a bounded sample of decode queries (host copies made before
-    each timed query)."""
-    import numpy as np
+    """The oracle as it stands, timed per query over the whole step: indexer over the query's
+    visible keys, top-k, and sparse attention for every layer of the index pass. Up to 32
+    queries of the workload are cycled (all of them for the long-context workloads). Host
+    copies of each query's inputs, and of the latent rows its selection gathers, are made
+    before the timing."""
     import torch
     import dsa_inputs as DI
     import oracle.dsa_oracle as O
@@ -144,21 +146,25 @@ def cpu_baseline(case, sets, budget_s):
 
     rows = DI.query_rows(case)
     d = sets[0]
-    host = []                     # host copies (float32) of what each sampled query reads
+    f = lambda x: x.detach().float().cpu().numpy()
+    host = []
     for t, b, p, base in rows[:32]:
-        f = lambda x: x.detach().float().cpu().numpy()
-        host.append((f(d["q_idx"][t]), f(d["k_idx"][base:base + p + 1]), f(d["w"][t]),
-                     f(d["q"][0][t]), f(d["kv"][0][base:base + p + 1])))
+        qI, kI, w = f(d["q_idx"][t]), f(d["k_idx"][base:base + p + 1]), f(d["w"][t])
+        sel = O.topk_row(O.indexer_scores_row(qI, kI, w), case.index_topk)
+        rows_dev = base + torch.as_tensor(sel[sel >= 0], device=d["kv"][0].device)
+        layers = [(f(d["q"][l][t]), f(d["kv"][l][rows_dev])) for l in range(case.layers)]
+        host.append((qI, kI, w, layers))
     done, spent = 0, 0.0
     stage = [0.0, 0.0, 0.0]
     while spent < budget_s and done < 100000:
-        qI, kI, w, q, kv = host[done % len(host)]
+        qI, kI, w, layers = host[done % len(host)]
         t0 = time.perf_counter()
         s = O.indexer_scores_row(qI, kI, w)
         t1 = time.perf_counter()
-        sel = O.topk_row(s, case.index_topk)
+        O.topk_row(s, case.index_topk)
         t2 = time.perf_counter()
-        O.sparse_attention_row(q, kv[sel[sel >= 0]], case.d_v, case.softmax_scale)
+        for q, kv_sel in layers:
+            O.sparse_attention_row(q, kv_sel, case.d_v, case.softmax_scale)
         t3 = time.perf_counter()
         stage = [stage[0] + t1 - t0, stage[1] + t2 - t1, stage[2] + t3 - t2]
         spent += t3 - t0
@@ -171,14 +177,16 @@ def cpu_baseline(case, sets, budget_s):
                 break
     except OSError:
         pass
+    lens = sorted({p + 1 for (_, _, p, _) in rows[:len(host)]})
+    ctx = f"{lens[0]}" if len(lens) == 1 else f"{lens[0]}..{lens[-1]}"
     return {"value": done / spent, "unit": "query-tokens/s", "cores": int(threads),
             "kind": "oracle", "cpu": model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "stage_seconds": {"indexer": round(stage[0], 3), "topk": round(stage[1], 3),
                               "attention": round(stage[2], 3)},
-            "sample": f"{done} decode queries of the same workload (full indexer over "
-                      f"{max(case.seqlens_k)} keys, top-{case.index_topk}, {case.n_heads}-head "
-                      f"sparse attention; {len(host)} distinct queries cycled), float64 NumPy, "
-                      f"{spent:.1f} s of oracle time"}
+            "sample": f"{done} query steps of the same workload ({len(host)} distinct queries "
+                      f"cycled, contexts {ctx}): indexer over every visible key, "
+                      f"top-{case.index_topk}, {case.n_heads}-head sparse attention for each of "
+                      f"{case.layers} layer(s); float64 NumPy, {spent:.1f} s of oracle time"}
 
 
 def main():
@@ -266,6 +274,17 @@ def main():
         if st:
             raise RuntimeError(f"libdsa call failed with status {st}")
 
+    def unshared_on(i, sp):
+        # the same layers with IndexShare off: every layer runs its own indexer + top-k pass (on
+        # the same indexer inputs, so the selection and outputs are unchanged)
+        st = 0
+        for l in range(case.layers):
+            st |= L.dsa_forward(batch.ptr, ctypes.byref(fargs[i % nsets][l]), idx.data_ptr(),
+                                1, outs[l].data_ptr(), lse.data_ptr(), fws.data_ptr(),
+                                fws.numel(), sp)
+        if st:
+            raise RuntimeError(f"libdsa call failed with status {st}")
+
     fused_on(0, sp)                  # first launches (code objects load) outside any capture
     step(0)
     torch.cuda.synchronize()
@@ -282,6 +301,8 @@ def main():
     for i in range(args.warmup):
         fused_on(i, sp)
         step(i)
+        if case.layers > 1:
+            unshared_on(i, sp)
         if graphs:
             graphs[i % nsets].replay()
     torch.cuda.synchronize()
@@ -294,6 +315,8 @@ def main():
                 graphs[(args.warmup + i) % nsets].replay()
             elif mode == "fused":
                 fused_on(args.warmup + i, sp)
+            elif mode == "unshared":
+                unshared_on(args.warmup + i, sp)
             else:
                 step(args.warmup + i)
         torch.cuda.synchronize()
@@ -304,6 +327,14 @@ def main():
     ms_eager = time_steps("fused")
     ms_separate = time_steps("separate")
     ms_graph = time_steps("graph") if graphs else None
+    index_share = None
+    if case.layers > 1:
+        ms_unshared = time_steps("unshared")
+        index_share = {"layers_per_index_pass": case.layers,
+                       "shared_ms_per_step": round(ms_eager, 5),
+                       "unshared_ms_per_step": round(ms_unshared, 5),
+                       "speedup": round(ms_unshared / ms_eager, 3),
+                       "what": "same step with every layer running its own indexer + top-k"}
     ms_step = ms_graph if args.launch == "graph" else ms_eager
     graph_info = None
     if graphs:
@@ -406,6 +437,7 @@ def main():
         "eager_ms_per_step": round(ms_eager, 5),
         "separate_calls_ms_per_step": round(ms_separate, 5),
         "graph": graph_info,
+        "index_share": index_share,
         "achieved_hbm_gbps": round(sb / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": sb,
         "kernel_ms": {"indexer": round(ms_idx, 5), "topk": round(ms_topk, 5),

@@ -22,7 +22,11 @@
  *   - All tensors are dense row-major device buffers owned by the caller. The library never
  *     allocates, frees or synchronises on a call path; each call only enqueues work on `stream`
  *     and returns. Scratch memory comes from a caller-provided workspace whose size is given by
- *     dsa_workspace_size(). The library keeps no mutable global state.
+ *     dsa_workspace_size(). The only mutable global state is one write-only device
+ *     array of the prefill indexer: lanes with no score to store (causally masked keys, keys or
+ *     queries past a sequence) store into it, so every key tile issues the same number of
+ *     stores; it is never read, so concurrent calls on several streams store into it without
+ *     affecting any result.
  *   - All argument checks run on the host before anything is enqueued; a non-zero status means
  *     nothing was launched. Device-resident values (cu_seqlens) cannot be checked without a
  *     synchronisation: the caller guarantees they are consistent with the host-side sizes, and
@@ -78,7 +82,8 @@ typedef struct {
  *   w      [T, index_n_heads]                  fp32
  *   scores [T, ld_scores]                      fp32, ld_scores >= max_seqlen_k
  * Products are accumulated in fp32; integer-valued inputs whose sums stay below 2^24 give
- * exact scores. */
+ * exact scores. q_idx, k_idx and w must be finite: the bf16 kernels are compiled without NaN
+ * semantics (the ReLU is a plain maximum), so a NaN or infinite input gives unspecified scores. */
 dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx,
                               const float* w, int32_t index_n_heads, int32_t index_head_dim,
                               dsa_dtype dtype, float* scores, int64_t ld_scores,

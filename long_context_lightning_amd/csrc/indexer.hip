@@ -265,8 +265,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void indexer_prefill_bf16(
   if (b >= nseq) return;
   const int q0 = cu_q[b];
   const int nq = cu_q[b + 1] - q0;
-  const int64_t kb0 = cu_k[b];
-  const int64_t kb1 = min(cu_k[b + 1], total_k);
+  // clamped like query_pos(): inconsistent cu_seqlens give wrong scores, never a read outside
+  // k_idx
+  const int64_t kb0 = max((int64_t)0, min(cu_k[b], total_k));
+  const int64_t kb1 = max(kb0, min(cu_k[b + 1], total_k));
   const int64_t L = kb1 - kb0;
   const int jb = blockIdx.x * PF_QB;
   if (jb >= nq || L <= 0 || q0 < 0 || q0 + nq > total_q) return;

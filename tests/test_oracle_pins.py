@@ -249,14 +249,37 @@ def pin_index_share():
     w = rng.integers(-2, 3, (T, 2)).astype(np.float64)
     qs = [rng.normal(size=(T, 3, 6)) for _ in range(4)]
     kvs = [rng.normal(size=(L, 6)) for _ in range(4)]
-    idx, outs = O.index_share(q_idx, k_idx, w, qs, kvs, cu_q, cu_k, 8, 4, 0.4)
-    for layer in range(4):
-        _, idx_l, attn_l = O.forward(q_idx, k_idx, w, qs[layer], kvs[layer], cu_q, cu_k, 8, 4, 0.4)
+    # count the (query, key) score pairs the indexer evaluates
+    import oracle.dsa_oracle as mod
+    pairs = [0]
+    real_row = mod.indexer_scores_row
+
+    def counting_row(q, k, w_):
+        pairs[0] += len(k)
+        return real_row(q, k, w_)
+
+    mod.indexer_scores_row = counting_row
+    try:
+        idx, outs = O.index_share(q_idx, k_idx, w, qs, kvs, cu_q, cu_k, 8, 4, 0.4)
+        shared_pairs = pairs[0]
+        pairs[0] = 0
+        per_layer = []
+        for layer in range(4):
+            per_layer.append(O.forward(q_idx, k_idx, w, qs[layer], kvs[layer], cu_q, cu_k, 8, 4,
+                                       0.4))
+        separate_pairs = pairs[0]
+    finally:
+        mod.indexer_scores_row = real_row
+    for layer, (_, idx_l, attn_l) in enumerate(per_layer):
         for t in range(T):
             assert np.array_equal(idx[t], idx_l[t])          # one selection for the group
             assert np.array_equal(outs[layer][t][0], attn_l[t][0])
-    # 4 layers sharing one indexer spend 1/4 of the indexer work: the 75% cut
-    assert 1 - 1 / 4 == 0.75
+    # causal pairs of the two queries (positions 49 and 39): 50 + 40. The group evaluates them
+    # once; one indexer per layer would evaluate them four times, so sharing cuts the indexer
+    # work by 75%
+    assert shared_pairs == 90
+    assert separate_pairs == 4 * 90
+    assert 1 - shared_pairs / separate_pairs == 0.75
 
 
 ALL_PINS = [pin_indexer_worked, pin_indexer_one_hot_closed_form, pin_indexer_relu_identity,

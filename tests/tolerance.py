@@ -1,9 +1,11 @@
 """Floating-point agreement bar for attention outputs.
 
-Both must hold per workload: max |gpu - ref| <= 2e-2 and the normwise relative error
-||gpu - ref||_F / ||ref||_F <= 1e-2. The normwise bound is the discriminating one: decode
-outputs have an element spread near 2e-3, so an all-zero output would meet the max-abs bound
-alone, while one wrong index out of 2048 moves the normwise error by about 3%.
+Both must hold for every query on its own (its [heads, d_v] output block): max |gpu - ref| <=
+2e-2 and the normwise relative error ||gpu - ref||_F / ||ref||_F <= 1e-2. The normwise bound is
+the discriminating one: decode outputs have an element spread near 2e-3, so an all-zero output
+would meet the max-abs bound alone, while one wrong index out of 2048 moves one query's
+normwise error by about 3%. Pooled over 32 queries the same mistake would move it by about
+0.55% and pass, so the bar is never applied to a stack of queries.
 """
 import numpy as np
 
