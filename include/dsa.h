@@ -127,6 +127,25 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void*
                               void* out, float* lse, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Step 3 without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Arguments,
+ * results and status codes are those of dsa_sparse_mla_fwd; the scratch that call keeps in the
+ * caller's workspace (each split's partial output and log-sum-exp) lives instead in a
+ * library-owned device array of DSA_NOALLOC_SCRATCH_BYTES on each GPU, which the GPU holds
+ * until the process ends. Nothing is allocated or freed. A call that would need more scratch
+ * than that (dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes) returns DSA_ERR_WORKSPACE with
+ * nothing enqueued. Every call on one GPU uses the same array and nothing in it needs to start
+ * at zero: calls ordered on one stream are safe, calls that overlap in time on one GPU (several
+ * streams or threads) race and give wrong results. The first call on a GPU looks the array's
+ * device address up (hipGetSymbolAddress, with that GPU current); make it before any graph
+ * capture that records this call. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status dsa_sparse_mla_fwd_noalloc(const dsa_batch* batch, const void* q, const void* kv,
+                                      const int32_t* indices, int32_t index_topk,
+                                      int32_t n_heads, int32_t d_qk, int32_t d_v,
+                                      float softmax_scale, dsa_dtype dtype, void* out, float* lse,
+                                      hipStream_t stream);
+
 /* Inputs of the three steps, for the fused call. */
 typedef struct {
   const void* q_idx;             /* [T, index_n_heads, index_head_dim]                         */

@@ -15,7 +15,8 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Batch", "indexer_scores", "topk", "sparse_mla_fwd", "forward", "workspace_size",
+__all__ = ["Batch", "indexer_scores", "topk", "sparse_mla_fwd", "sparse_mla_fwd_noalloc",
+           "forward", "workspace_size",
            "check_batch", "lib", "LIB_PATH", "DsaError", "OP_INDEXER", "OP_TOPK",
            "OP_SPARSE_MLA", "OP_FORWARD"]
 
@@ -70,6 +71,10 @@ def _lib_handle():
                                          _c.c_int32, _c.c_float, _c.c_int, _vp, _vp, _vp,
                                          _c.c_size_t, _vp]
         L.dsa_sparse_mla_fwd.restype = st
+        L.dsa_sparse_mla_fwd_noalloc.argtypes = [B, _vp, _vp, _vp, _c.c_int32, _c.c_int32,
+                                                 _c.c_int32, _c.c_int32, _c.c_float, _c.c_int,
+                                                 _vp, _vp, _vp]
+        L.dsa_sparse_mla_fwd_noalloc.restype = st
         L.dsa_forward.argtypes = [B, _c.POINTER(_CForwardArgs), _vp, _c.c_int32, _vp, _vp, _vp,
                                   _c.c_size_t, _vp]
         L.dsa_forward.restype = st
@@ -223,6 +228,26 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, bat
         float(softmax_scale), _dtype_code(q), out.data_ptr(),
         lse.data_ptr() if lse is not None else None,
         ws.data_ptr() if ws is not None else None, nb, _stream(q)), "dsa_sparse_mla_fwd")
+    return out, lse
+
+
+def sparse_mla_fwd_noalloc(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                           batch: Batch, softmax_scale: float, d_v: int, out: torch.Tensor,
+                           lse: Optional[torch.Tensor] = None):
+    """``sparse_mla_fwd`` into caller-provided ``out`` (and ``lse``) with the library's own
+    per-GPU scratch: no workspace is passed and nothing is allocated."""
+    T = batch.total_q
+    _need(q, "q", (T, None, None))
+    H, d_qk = q.shape[1], q.shape[2]
+    _need(kv, "kv", (batch.total_k, d_qk), q.dtype)
+    _need(indices, "indices", (T, None), torch.int32)
+    _need(out, "out", (T, H, d_v), q.dtype)
+    if lse is not None:
+        _need(lse, "lse", (T, H), torch.float32)
+    _check(_lib_handle().dsa_sparse_mla_fwd_noalloc(
+        batch.ptr, q.data_ptr(), kv.data_ptr(), indices.data_ptr(), indices.shape[1], H, d_qk,
+        d_v, float(softmax_scale), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q)), "dsa_sparse_mla_fwd_noalloc")
     return out, lse
 
 

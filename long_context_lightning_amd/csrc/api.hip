@@ -1,6 +1,7 @@
 // C ABI of libdsa: host-side validation, workspace layout and launch sequencing.
 // Every check runs before anything is enqueued; calls only enqueue work on the caller's stream.
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dsa.h"
@@ -8,7 +9,42 @@
 
 using dsa::Batch;
 
+// Scratch of dsa_sparse_mla_fwd_noalloc (the split partials of the sparse-MLA kernel), one copy
+// per GPU, held until the process ends. In host code this name stands for the symbol, not for a
+// device address: the address on each GPU comes from hipGetSymbolAddress (noalloc_scratch()).
+static __device__ __align__(256) char dsa_noalloc_scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of dsa_noalloc_scratch, per device
+
+// Device address of the scratch array on the device of `stream`, looked up once per device with
+// that device current.
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(dsa_noalloc_scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -133,6 +169,30 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void*
   return from_hip(dsa::launch_sparse_mla_f32(b, (const float*)q, (const float*)kv, indices,
                                              index_topk, n_heads, d_qk, d_v, softmax_scale,
                                              (float*)out, lse, stream));
+}
+
+dsa_status dsa_sparse_mla_fwd_noalloc(const dsa_batch* batch, const void* q, const void* kv,
+                                      const int32_t* indices, int32_t index_topk,
+                                      int32_t n_heads, int32_t d_qk, int32_t d_v,
+                                      float softmax_scale, dsa_dtype dtype, void* out, float* lse,
+                                      hipStream_t stream) {
+  dsa_status st = check_mla(batch, q, kv, indices, index_topk, n_heads, d_qk, d_v,
+                            softmax_scale, dtype, out);
+  if (st != DSA_OK) return st;
+  if (dtype != DSA_BF16)     // the fp32 kernel uses no scratch
+    return dsa_sparse_mla_fwd(batch, q, kv, indices, index_topk, n_heads, d_qk, d_v,
+                              softmax_scale, dtype, out, lse, nullptr, 0, stream);
+  const Batch b = to_batch(batch);
+  const dsa::MlaPlan plan = dsa::plan_sparse_mla_bf16(b, index_topk, n_heads);
+  if (plan.workspace > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  if (batch->total_q == 0) return DSA_OK;
+  void* scratch = nullptr;
+  if (plan.workspace > 0) {
+    const hipError_t e = noalloc_scratch(stream, &scratch);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  }
+  return from_hip(dsa::launch_sparse_mla_bf16(b, q, kv, indices, index_topk, n_heads,
+                                              softmax_scale, out, lse, scratch, plan, stream));
 }
 
 size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,

@@ -128,3 +128,20 @@ def test_workspace_sizes(L):
     fwd = ws(3, ctypes.byref(b), 2048, 64, 512)
     assert fwd >= 2 * 60 * 4 + ws(2, ctypes.byref(b), 2048, 64, 512)
     assert ws(2, ctypes.byref(b), 2048, 8, 64) == 0      # fp32 path needs no split scratch
+
+
+def test_sparse_mla_noalloc_rejects_bad_arguments(L):
+    """The no-workspace sparse-MLA call validates like the workspace call, on the host, before
+    it looks up its device scratch (nothing here reaches a GPU)."""
+    b = _batch()
+    f = L.dsa_sparse_mla_fwd_noalloc
+    args = [ctypes.byref(b), FAKE, FAKE, FAKE, 2048, 64, 576, 512, 1 / 24, 1, FAKE, None, None]
+    a = list(args); a[1] = None
+    assert f(*a) == INVALID
+    a = list(args); a[10] = None                 # no output buffer
+    assert f(*a) == INVALID
+    a = list(args); a[5] = 48
+    assert f(*a) == UNSUPPORTED
+    a = list(args); a[8] = float("nan")
+    assert f(*a) == INVALID
+    assert f(None, *args[1:]) == INVALID
