@@ -113,9 +113,7 @@ __device__ __forceinline__ float* stat(char* stage, int i) {
   return (float*)(stage + (i >> 5) * ROWB + ROPE_OFF + (i & 31) * 4);
 }
 constexpr int ST_MAX = 0;       // [8 waves][HG] maximum over each wave's 16 rows
-constexpr int ST_SUM = 256;     // [8 waves][HG] sums over the same rows
 constexpr int ST_FLAG = 512;    // [8]           wave saw a logit beyond its reference headroom
-constexpr int ST_FAC = 576;     // [2][HG]       rescale factors of raised references
 
 // Element r of the QK accumulator kept by K-half wave kh after the exchange: value q (0..7) of
 // the wave is element 8*(q/4) + 4*kh + q%4; the other eight go to the partner wave.
@@ -201,7 +199,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   // output block. Only if a later tile exceeds a reference by more than 2^kHeadroom is it raised,
   // with the head's output block and running sum scaled by exp2(old - new) (online softmax).
   f32x16 o[VB_WAVE];
-  float l_run = 0.f;
+  float l_part = 0.f;             // this wave's share (its rows) of the softmax sum of head c32
   // reference maxima of head c32 in both head halves: every wave tracks both and updates them
   // from the same shared statistics, so every decision on them is uniform across the workgroup
   float mref0 = -INFINITY, mref1 = -INFINITY;
@@ -273,11 +271,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       wait_all_memory();
       vm_even = __ballot((uint32_t)masked(0, i_even) < Lu);
       vm_odd = __ballot((uint32_t)masked(1, i_odd) < Lu);
-      issue(stage0, 0, i_even);
       // The query block [64 heads x 576] has the shape of a tile: it is gathered the same way,
       // coalesced, into stage 1 (the upper half of the last group of an odd number of 32-head
       // groups reads heads 0..31 again), and each wave reads its B operands from there with
-      // the same conflict-free pattern as the QK A operands.
+      // the same conflict-free pattern as the QK A operands. It goes out first and tile 0
+      // right behind it; loads complete in issue order, so the query block is read into
+      // registers while tile 0 still streams in, and tile 1 follows into stage 1 at once.
       {
         int tt = tid;
         opaque(tt);
@@ -291,8 +290,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
                    stage1 + (j * NTHREADS + wave * 64) * 16);
         }
       }
-      wait_all_memory();                       // tile 0 and the query block
-      __syncthreads();
+      issue(stage0, 0, i_even);
+      wait_vmcnt<LOADS_PER_THREAD>();          // this wave's query-block gathers
+      __syncthreads();                         // every wave's
       {
         const int row = hl * HG + c32;
         const int sq = swz(row);
@@ -306,8 +306,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         for (int i = 0; i < QK_STEPS; ++i) asm volatile("" : "+v"(qreg[i]));
       }
       __syncthreads();
-      // tile 1 streams in while tile 0 computes
-      if (1 < ntiles) issue(stage1, 1, i_odd);
+      // tile 1 streams in while tile 0 lands and computes
+      if (1 < ntiles) {
+        issue(stage1, 1, i_odd);
+        wait_vmcnt<LOADS_PER_THREAD>();        // tile 0 (tile 1 may still be in flight)
+      } else {
+        wait_all_memory();
+      }
+      __syncthreads();                         // tile 0 published
     }
 
     // A-operand lane bases: step i reads chunk 36*kh + 2*i + half of row 32*rb + c32; with
@@ -322,7 +328,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
                  (((2 * (u & 3) + half) ^ sw) << 4);
     }
 
-    const int w0 = 4 * hl;                     // first wave of this head half
     auto tile_max = [&](char* stage, int h) __attribute__((always_inline)) -> float {
       return fmaxf(fmaxf(*stat(stage, ST_MAX + (4 * h + 0) * HG + c32), *stat(stage, ST_MAX + (4 * h + 1) * HG + c32)),
                    fmaxf(*stat(stage, ST_MAX + (4 * h + 2) * HG + c32), *stat(stage, ST_MAX + (4 * h + 3) * HG + c32)));
@@ -342,23 +347,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       if (mref0 == -INFINITY || r0) mref0 = mt0;
       if (mref1 == -INFINITY || r1) mref1 = mt1;
       if (__ballot(r0 || r1) != 0) {           // uniform across the workgroup
-        if (wave == 0 && half == 0) {
-          *stat(stage, ST_FAC + c32) = f0;
-          *stat(stage, ST_FAC + HG + c32) = f1;
-        }
-        __syncthreads();
+        // every value a lane holds belongs to its own head (hl, c32)
+        const float f = hl ? f1 : f0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float f = *stat(stage, ST_FAC + hl * HG + mfma32_row(r, lane));
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
           for (int db = 0; db < VB_WAVE; ++db) o[db][r] *= f;
-        }
-        l_run *= hl ? f1 : f0;
+        l_part *= f;
       }
     };
-    // probabilities exp2(s - m_ref) of this wave's 16 rows for head c32 into P (bf16) and
-    // their sum into the statistics
-    auto write_p = [&](char* stage, const float (&sv)[8]) __attribute__((always_inline)) {
+    // probabilities exp2(s - m_ref) of this wave's 16 rows for head c32 into P (bf16); returns
+    // their sum
+    auto write_p = [&](const float (&sv)[8]) __attribute__((always_inline)) -> float {
       const float m_ref = hl ? mref1 : mref0;
       const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       float ls = 0.f;
@@ -375,8 +375,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         // rows 32*rb + 16*g + 8*kh + 4*half + e of head c32
         *(bf16x4*)(rbuf + (wave ^ 1) * XSLOT + (g * HG + c32) * 16 + half * 8) = pk;
       }
-      ls = halves_sum(ls);
-      if (half == 0) *stat(stage, ST_SUM + wave * HG + c32) = ls;
+      return halves_sum(ls);
     };
 
     // One tile in stage `stage`; idx holds the indices of this tile and receives those of
@@ -462,7 +461,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       // the probabilities.
       const bool need_max = __ballot(mref0 == -INFINITY || mref1 == -INFINITY) != 0;
       if (need_max) update_refs(stage, mx);
-      write_p(stage, sv);
+      float ls = write_p(sv);
       const float m_ref = hl ? mref1 : mref0;
       const bool exceed = !need_max && mx > m_ref + kHeadroom;
       const bool wave_exceeds = __ballot(exceed) != 0;   // ballot with every lane active
@@ -473,11 +472,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       for (int w = 0; w < NWAVES; ++w) flags += *stat(stage, ST_FLAG + w);
       if (flags != 0.f) {                      // uniform: raise, rescale, redo the probabilities
         update_refs(stage, mx);
-        write_p(stage, sv);
+        ls = write_p(sv);
         __syncthreads();
       }
-      l_run += (*stat(stage, ST_SUM + (w0 + 0) * HG + c32) + *stat(stage, ST_SUM + (w0 + 1) * HG + c32)) +
-               (*stat(stage, ST_SUM + (w0 + 2) * HG + c32) + *stat(stage, ST_SUM + (w0 + 3) * HG + c32));
+      l_part += ls;
 
       // ---- O[32 heads x 128 cols] += P[32 heads x 64 rows] * V[64 rows x 128 cols]
       // V[krow][col] for the B operand of value block blk (32 columns), rows 4*rr.. of the
@@ -511,7 +509,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
             const int blk = VB_WAVE * cq + db;
             const i16x4 v0 = lds_read_tr16(vb[0][db & 1] + ks * 16 * ROWB + (blk << 6));
             const i16x4 v1 = lds_read_tr16(vb[1][db & 1] + ks * 16 * ROWB + (blk << 6));
-            o[db] = mfma32x32x16(pa, concat_bf16(v0, v1), o[db]);
+            o[db] = mfma32x32x16(concat_bf16(v0, v1), pa, o[db]);
           }
         }
       }
@@ -532,58 +530,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   }
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
-  float* fin = (float*)rbuf;                   // [0,64): l per head, [64,128): max per head
+  // [0,256): each wave's share of the sum per head ([w4][64 heads]), [256,320): max per head,
+  // [320,384): sum per head
+  float* fin = (float*)rbuf;
   __syncthreads();
-  if (w4 == 0 && half == 0) {
-    fin[hl * HG + c32] = l_run;
-    fin[WG_HEADS + hl * HG + c32] = hl ? mref1 : mref0;
-  }
+  if (half == 0) fin[w4 * WG_HEADS + hl * HG + c32] = l_part;
+  if (w4 == 0 && half == 0) fin[4 * WG_HEADS + hl * HG + c32] = hl ? mref1 : mref0;
   __syncthreads();
-  float inv[16];
+  if (tid < WG_HEADS)
+    fin[5 * WG_HEADS + tid] = (fin[tid] + fin[WG_HEADS + tid]) +
+                              (fin[2 * WG_HEADS + tid] + fin[3 * WG_HEADS + tid]);
+  __syncthreads();
+  // Every value a lane holds belongs to head (hl, c32): element r of value block db is column
+  // 32*(VB_WAVE*cq + db) + 8*(r/4) + 4*half + r%4, so each group of four elements is four
+  // consecutive columns of the head's output row. The normalised [64 heads x 512] block is
+  // staged in LDS as 8-byte pieces (rows padded to OT_PITCH bytes, so the 32 heads of a store
+  // fall on distinct bank pairs), then written with 16-byte stores, each wave instruction 1 KB
+  // of one row: the final output with one split, else this split's partial output (the same
+  // row-major layout, one block per split), which the merge kernel streams back.
+  {
+    constexpr int OT_PITCH = DV * 2 + 16;
+    static_assert(WG_HEADS * OT_PITCH <= STAGE_BYTES, "the staged block fits one stage");
+    const float l = fin[5 * WG_HEADS + hl * HG + c32];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    char* orow_lds = stage0 + (hl * HG + c32) * OT_PITCH + (VB_WAVE * cq * 32 + 4 * half) * 2;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float l = fin[hl * HG + mfma32_row(r, lane)];
-    inv[r] = l > 0.f ? 1.f / l : 0.f;
-  }
-  const int nhg32 = H / HG;
-  if (nsplit > 1) {
-    // partial output in the accumulator layout: per (wave, value block) each lane stores its
-    // 16 values as 32 contiguous bytes, so a wave writes 2 KB contiguous per block
-    if (heads_valid) {
-      __bf16* po = part_o + ((((int64_t)t * nsplit + split) * nhg32 + g32) * 4 + w4) *
-                                (VB_WAVE * 1024);
+    for (int db = 0; db < VB_WAVE; ++db)
 #pragma unroll
-      for (int db = 0; db < VB_WAVE; ++db) {
-        bf16x8 lo8, hi8;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          lo8[r] = (__bf16)(o[db][r] * inv[r]);
-          hi8[r] = (__bf16)(o[db][8 + r] * inv[8 + r]);
-        }
-        *(bf16x8*)(po + (db * 64 + lane) * 16) = lo8;
-        *(bf16x8*)(po + (db * 64 + lane) * 16 + 8) = hi8;
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * g + e] * inv);
+        *(bf16x4*)(orow_lds + (db * 32 + 8 * g) * 2) = v;
       }
-    }
-  } else {
-    // final output: transpose the [64 heads x 512] block through LDS, then 16-byte stores
-    __bf16* ot = (__bf16*)stage0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = hl * HG + mfma32_row(r, lane);
-#pragma unroll
-      for (int db = 0; db < VB_WAVE; ++db)
-        ot[hr * DV + (VB_WAVE * cq + db) * 32 + c32] = (__bf16)(o[db][r] * inv[r]);
-    }
     __syncthreads();
-    __bf16* ob = out + ((int64_t)t * H + hg * WG_HEADS) * DV;
-    const int heads = min(WG_HEADS, H - hg * WG_HEADS);
-    const int pieces = heads * DV / 8;
-    for (int piece = tid; piece < pieces; piece += NTHREADS)
-      *(bf16x8*)(ob + piece * 8) = *(const bf16x8*)(ot + piece * 8);
+    __bf16* ob = (nsplit == 1 ? out + (int64_t)t * H * DV
+                              : part_o + ((int64_t)t * nsplit + split) * H * DV) +
+                 (int64_t)hg * WG_HEADS * DV;
+    const int pieces = min(WG_HEADS, H - hg * WG_HEADS) * (DV / 8);
+    for (int piece = tid; piece < pieces; piece += NTHREADS) {
+      const int row = piece >> 6, c = piece & 63;
+      *(bf16x8*)(ob + piece * 8) = *(const bf16x8*)(stage0 + row * OT_PITCH + c * 16);
+    }
   }
   if (w4 == 0 && half == 0 && heads_valid) {
-    const float l = fin[hl * HG + c32];
-    const float val = l > 0.f ? (fin[WG_HEADS + hl * HG + c32] + log2f(l)) * kLn2 : -INFINITY;
+    const float l = fin[5 * WG_HEADS + hl * HG + c32];
+    const float val = l > 0.f ? (fin[4 * WG_HEADS + hl * HG + c32] + log2f(l)) * kLn2 : -INFINITY;
     const int64_t h = g32 * HG + c32;
     if (nsplit == 1) {
       if (lse) lse[(int64_t)t * H + h] = val;
@@ -593,124 +585,73 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   }
 }
 
-// Merges the splits of one (query, 32-head group, wave, value block): the block's 1024 outputs
-// are the 16 (head, column) values that each of 64 lanes holds in the sparse kernel's
-// accumulator layout. out = sum_i exp(lse_i - lse) * o_i with lse = logsumexp_i lse_i
-// (natural-log units). Four waves share the splits (wave q takes splits q, q+4, ..); each lane
-// issues all loads of a pass before the weights are known, and the four partial sums meet in
-// LDS. SPW splits per wave and pass (chosen from the split count, so a pass rarely loads a
-// split twice): every load of a pass is issued unconditionally (the split index clamped), so
-// the compiler counts them and waits for the log-sum-exps alone, which are loaded first.
+// Merges the splits of every (query, head): out = sum_i exp(lse_i - lse) * o_i with
+// lse = logsumexp_i lse_i (natural-log units), o_i the normalised partial outputs. P adjacent
+// threads share one piece of 8 consecutive output columns (64 pieces per head); thread p takes
+// splits p, p+P, .. (at most CMB_SPLITS of them) and issues all their partial and log-sum-exp
+// loads at once, so a merge is one memory round trip; maxima, sums and the weighted partial sums
+// then meet across the P threads with lane exchanges.
 constexpr int CMB_THREADS = 256;
+constexpr int CMB_SPLITS = 8;
 
-template <int SPW>
+template <int P>
 __global__ __launch_bounds__(CMB_THREADS) void mla_combine(const __bf16* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
-                                                           int nsplit, int H,
+                                                           int nsplit, int H, int total_q,
                                                            __bf16* __restrict__ out,
                                                            float* __restrict__ lse) {
-  extern __shared__ float wgt[];               // [nsplit][32] merge weights per head
-  __shared__ float red[3][16][WAVE];           // partial sums of waves 1..3
-  __shared__ float mred[8][32], sred[8][32];   // per-head maximum / sum of eight threads
-  __shared__ __attribute__((aligned(16))) __bf16 ot[32][40];   // output block, row = head
-  const int t = blockIdx.x;
-  const int y = blockIdx.y;
-  const int db = y % VB_WAVE;
-  const int w = (y / VB_WAVE) % 4;
-  const int g32 = y / (VB_WAVE * 4);
-  const int nhg32 = H / HG;
-  const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
-  const int wv = tid >> 6;
-  const int h0 = g32 * HG;                     // first head of this group
-  const int64_t stride = (int64_t)nhg32 * 4 * VB_WAVE * 1024;     // elements per (t, split)
-  const __bf16* po = part_o + (int64_t)t * nsplit * stride + ((g32 * 4 + w) * VB_WAVE + db) * 1024 +
-                     lane * 16;
-  bf16x8 lo8[SPW], hi8[SPW];
-  auto load = [&](int base) {
+  const int64_t gid = (int64_t)blockIdx.x * CMB_THREADS + threadIdx.x;
+  const int p = (int)(gid & (P - 1));
+  const int64_t piece = gid / P;
+  const int c8 = (int)(piece & 63);            // columns 8*c8 .. 8*c8+7
+  const int64_t th = piece >> 6;               // t * H + h
+  if (th >= (int64_t)total_q * H) return;      // all P threads of a piece together
+  const int64_t t = th / H;
+  const int64_t h = th - t * H;
+  const float* pl = part_lse + t * nsplit * H + h;                 // split i at pl[i * H]
+  const __bf16* po = part_o + (t * nsplit * H + h) * DV + c8 * 8;  // split i at po[i * H * DV]
+  bf16x8 v[CMB_SPLITS];
+  float li[CMB_SPLITS];
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int i = min(base + wv + 4 * j, nsplit - 1);   // a clamped copy is loaded, not used
-      lo8[j] = *(const bf16x8*)(po + i * stride);
-      hi8[j] = *(const bf16x8*)(po + i * stride + 8);
-    }
-  };
-  // every split's log-sum-exp of the group's 32 heads. The first one per thread is loaded
-  // before the partial outputs and stored after them: loads complete in issue order, so the
-  // merge weights are computed while the partials are still streaming in.
-  const int nl = nsplit * 32;
-  const float lse_first = tid < nl ? part_lse[((int64_t)t * nsplit + (tid >> 5)) * H + h0 + (tid & 31)]
-                                   : 0.f;
-  load(0);
-  if (tid < nl) wgt[tid] = lse_first;
-  for (int j = tid + CMB_THREADS; j < nl; j += CMB_THREADS)
-    wgt[j] = part_lse[((int64_t)t * nsplit + (j >> 5)) * H + h0 + (j & 31)];
-  __syncthreads();
-  // merge weights exp(lse_i - lse): eight threads per head, each over every eighth split, the
-  // maximum and the sum meeting in LDS (base-2 hardware exponent and logarithm)
-  {
-    const int hh = tid & 31, g = tid >> 5;
-    float m = -INFINITY;
-    for (int i = g; i < nsplit; i += 8) m = fmaxf(m, wgt[i * 32 + hh]);
-    mred[g][hh] = m;
-    __syncthreads();
-    m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, mred[j][hh]);
-    const float m2 = m * kLog2e;
-    float sum = 0.f;
-    if (m != -INFINITY)
-      for (int i = g; i < nsplit; i += 8)
-        sum += __builtin_amdgcn_exp2f(wgt[i * 32 + hh] * kLog2e - m2);
-    sred[g][hh] = sum;
-    __syncthreads();
-    sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += sred[j][hh];
-    const float tot2 = m2 + __builtin_amdgcn_logf(sum);   // log2 units; sum >= 1
-    for (int i = g; i < nsplit; i += 8) {
-      const float li = wgt[i * 32 + hh];
-      wgt[i * 32 + hh] = (li == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(li * kLog2e - tot2);
-    }
-    if (lse && w == 0 && db == 0 && g == 0)
-      lse[(int64_t)t * H + h0 + hh] = (m == -INFINITY) ? -INFINITY : tot2 * kLn2;
+  for (int j = 0; j < CMB_SPLITS; ++j) {       // past the last split: a clamped copy, unused
+    const int i = min(p + j * P, nsplit - 1);
+    v[j] = *(const bf16x8*)(po + (int64_t)i * H * DV);
+    li[j] = pl[(int64_t)i * H];
   }
-  __syncthreads();
-  float acc[16];
+  float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int base = 0;;) {
+  for (int j = 0; j < CMB_SPLITS; ++j)
+    if (p + j * P < nsplit) m = fmaxf(m, li[j]);
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int i = base + wv + 4 * j;
-      if (i < nsplit) {
+  for (int o = 1; o < P; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+  const float m2 = m * kLog2e;
+  float e[CMB_SPLITS], sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          acc[r] += wgt[i * 32 + mfma32_row(r, lane)] * (float)lo8[j][r];
-          acc[8 + r] += wgt[i * 32 + mfma32_row(8 + r, lane)] * (float)hi8[j][r];
-        }
-      }
-    }
-    base += 4 * SPW;
-    if (base >= nsplit) break;
-    load(base);
+  for (int j = 0; j < CMB_SPLITS; ++j) {
+    e[j] = (p + j * P < nsplit && li[j] != -INFINITY) ? __builtin_amdgcn_exp2f(li[j] * kLog2e - m2)
+                                                       : 0.f;
+    sum += e[j];
   }
-  if (wv > 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wv - 1][r][lane] = acc[r];
-  }
-  __syncthreads();
-  if (wv == 0) {
-    // the [32 heads x 32 columns] block is transposed through LDS (in order within the wave),
-    // then each lane stores 32 contiguous bytes of one head's row
+  for (int o = 1; o < P; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
+  // sum >= 1 when m is finite (the maximal split contributes exp2(0))
+  const float inv = m != -INFINITY ? 1.f / sum : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      ot[mfma32_row(r, lane)][lane & 31] =
-          (__bf16)(acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane]);
-    const int row = lane >> 1, c0 = (lane & 1) * 16;
-    __bf16* ob = out + ((int64_t)t * H + h0 + row) * DV + (VB_WAVE * w + db) * 32 + c0;
-    *(bf16x8*)ob = *(const bf16x8*)&ot[row][c0];
-    *(bf16x8*)(ob + 8) = *(const bf16x8*)&ot[row][c0 + 8];
+  for (int j = 0; j < CMB_SPLITS; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(e[j], (float)v[j][c], acc[c]);
+#pragma unroll
+  for (int o = 1; o < P; o <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], o, WAVE);
+  if (p == 0) {
+    bf16x8 r;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r[c] = (__bf16)(acc[c] * inv);
+    *(bf16x8*)(out + th * DV + c8 * 8) = r;
+    if (lse && c8 == 0)
+      lse[th] = m == -INFINITY ? -INFINITY : (m2 + __builtin_amdgcn_logf(sum)) * kLn2;
   }
 }
 
@@ -814,17 +755,24 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
       part_o, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  const dim3 cgrid(b.total_q, (n_heads / HG) * 4 * VB_WAVE);
-  const size_t csmem = plan.nsplit * 32 * sizeof(float);
-  if (plan.nsplit <= 8)
-    mla_combine<2><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
-                                                          (__bf16*)out, lse);
-  else if (plan.nsplit <= 16)
-    mla_combine<4><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
-                                                          (__bf16*)out, lse);
-  else
-    mla_combine<8><<<cgrid, CMB_THREADS, csmem, stream>>>(part_o, part_lse, plan.nsplit, n_heads,
-                                                          (__bf16*)out, lse);
+  // P threads per 8-column piece, each merging at most CMB_SPLITS splits
+  int P = 1;
+  while (P * CMB_SPLITS < plan.nsplit) P *= 2;
+  const int64_t cthreads = (int64_t)b.total_q * n_heads * (DV / 8) * P;
+  const dim3 cgrid((unsigned)((cthreads + CMB_THREADS - 1) / CMB_THREADS));
+  auto cmb = [&](auto kern) {
+    kern<<<cgrid, CMB_THREADS, 0, stream>>>(part_o, part_lse, plan.nsplit, n_heads, b.total_q,
+                                            (__bf16*)out, lse);
+  };
+  switch (P) {
+    case 1: cmb(mla_combine<1>); break;
+    case 2: cmb(mla_combine<2>); break;
+    case 4: cmb(mla_combine<4>); break;
+    case 8: cmb(mla_combine<8>); break;
+    case 16: cmb(mla_combine<16>); break;
+    case 32: cmb(mla_combine<32>); break;
+    default: cmb(mla_combine<64>); break;
+  }
   return hipGetLastError();
 }
 
