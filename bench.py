@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b32_l16k")
+    ap.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="element type of the indexer inputs q_I / k_I (fp8: OCP e4m3fn; the "
+                         "attention stays bf16)")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -49,25 +52,26 @@ def parse():
     return ap.parse_args()
 
 
-def step_bytes(case):
+def step_bytes(case, ib=2):
     """Algorithmic HBM bytes of one step: every key row of the indexer cache, the selected
-    latent rows, queries, outputs, indexer queries and weights (intermediates excluded)."""
+    latent rows, queries, outputs, indexer queries and weights (intermediates excluded); ib =
+    bytes per indexer element (2 for bf16, 1 for fp8)."""
     import dsa_inputs as DI
     tot = 0
     for t, b, p, base in DI.query_rows(case):
         n = p + 1
-        tot += n * case.index_head_dim * 2                                  # k_I rows
+        tot += n * case.index_head_dim * ib                                 # k_I rows
         tot += min(case.index_topk, n) * case.d_qk * 2 * case.layers        # gathered rows
         tot += case.n_heads * (case.d_qk + case.d_v) * 2 * case.layers      # q in, out
-        tot += case.index_n_heads * (case.index_head_dim * 2 + 4)           # q_I, w
+        tot += case.index_n_heads * (case.index_head_dim * ib + 4)          # q_I, w
     return tot
 
 
-def indexer_bytes(case):
+def indexer_bytes(case, ib=2):
     import dsa_inputs as DI
     tot = 0
     for t, b, p, base in DI.query_rows(case):
-        tot += (p + 1) * case.index_head_dim * 2 + case.index_n_heads * (case.index_head_dim * 2 + 4)
+        tot += (p + 1) * case.index_head_dim * ib + case.index_n_heads * (case.index_head_dim * ib + 4)
     return tot
 
 
@@ -205,12 +209,19 @@ def main():
     # A step touches step_bytes(case) of its input set (the whole indexer key cache, only the
     # selected latent rows). Between two uses of one set the other sets touch at least 1 GiB,
     # four times the Infinity Cache, so no step is served from an earlier step's cached lines.
-    touched = step_bytes(case)
+    fp8 = args.index_dtype == "fp8"
+    touched = step_bytes(case, 1 if fp8 else 2)
     nsets = args.sets or max(2, 1 + math.ceil((1 << 30) / touched))
     sets = []
     for i in range(nsets):
         c = DI.Case(**{**case.__dict__, "seed_base": case.seed_base + 100 * i})
-        sets.append(DI.make_inputs(c, "cuda"))
+        d = DI.make_inputs(c, "cuda")
+        if fp8:        # integer-valued indexer inputs are exact in e4m3fn
+            for key in ("q_idx", "k_idx"):
+                v = d[key].to(torch.float8_e4m3fn)
+                assert torch.equal(v.float(), d[key].float())
+                d[key] = v
+        sets.append(d)
     d0 = sets[0]
     batch = dsa.Batch(d0["cu_seqlens_q"], d0["cu_seqlens_k"], max(case.seqlens_q),
                       max(case.seqlens_k), case.total_q, case.total_k)
@@ -234,7 +245,8 @@ def main():
     fargs = [[dsa._CForwardArgs(d["q_idx"].data_ptr(), d["k_idx"].data_ptr(), d["w"].data_ptr(),
                                 case.index_n_heads, case.index_head_dim, case.index_topk,
                                 d["q"][l].data_ptr(), d["kv"][l].data_ptr(), case.n_heads,
-                                case.d_qk, case.d_v, case.softmax_scale, 1)
+                                case.d_qk, case.d_v, case.softmax_scale, 1, 1 if fp8 else 0,
+                                None)
               for l in range(case.layers)] for d in sets]
 
     def fused_on(i, sp):
@@ -248,6 +260,15 @@ def main():
         if st:
             raise RuntimeError(f"libdsa call failed with status {st}")
 
+    def idx_on(d, sp):
+        if fp8:
+            return L.dsa_indexer_scores_fp8(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
+                                            None, d["w"].data_ptr(), case.index_n_heads,
+                                            case.index_head_dim, scores.data_ptr(), ld, sp)
+        return L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
+                                    d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
+                                    1, scores.data_ptr(), ld, sp)
+
     def step(i, ev=None):
         step_on(i, sp, ev)
 
@@ -255,9 +276,7 @@ def main():
         d = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
-        st = L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
-                                  d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
-                                  1, scores.data_ptr(), ld, sp)
+        st = idx_on(d, sp)
         if ev is not None:
             ev[1].record(stream)
         st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
@@ -376,10 +395,7 @@ def main():
         return e0.elapsed_time(e1) / args.steps
 
     def idx_call(i):
-        d = sets[i % nsets]
-        return L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
-                                    d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
-                                    1, scores.data_ptr(), ld, sp)
+        return idx_on(sets[i % nsets], sp)
 
     def mla_call(i):
         d, l = sets[i % nsets], i % case.layers
@@ -396,8 +412,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    sb = step_bytes(case)
-    ib, mb = indexer_bytes(case), mla_bytes(case) // case.layers
+    eb = 1 if fp8 else 2
+    sb = step_bytes(case, eb)
+    ib, mb = indexer_bytes(case, eb), mla_bytes(case) // case.layers
     kern = {"indexer": (launch_ms["indexer"], ib), "sparse_mla": (launch_ms["sparse_mla"], mb)}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
@@ -408,13 +425,13 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
+                "traffic": traffic_record(args.workload + ("_fp8" if fp8 else ""), dom), "traffic_unit": "B/launch",
                 "algorithmic_flops_per_launch": dflops, "avg_launch_ms": round(dms, 5)}
     else:
         achieved = dbytes / (dms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_record(args.workload, dom), "traffic_unit": "B/launch",
+                "traffic": traffic_record(args.workload + ("_fp8" if fp8 else ""), dom), "traffic_unit": "B/launch",
                 "algorithmic_bytes_per_launch": dbytes,
                 "avg_launch_ms": round(dms, 5)}
     line = {
@@ -424,7 +441,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if case.dtype.__str__().endswith("bfloat16") else "f32",
+        "dtype": ("bf16+fp8" if fp8 else "bf16") if case.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{case.name}: {case.batch} sequences, contexts "
                                f"{min(case.seqlens_k)}..{max(case.seqlens_k)}, "
@@ -433,6 +450,7 @@ def main():
                                f"{case.n_heads}-head MQA over {case.d_qk}-wide latent "
                                f"({case.d_v} value), {case.layers} layer(s) per index pass",
                    "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets,
+                   "indexer_inputs": "fp8 e4m3fn" if fp8 else case.dtype.__str__()[6:],
                    "launch": "hip_graph" if args.launch == "graph" else "eager"},
         "eager_ms_per_step": round(ms_eager, 5),
         "separate_calls_ms_per_step": round(ms_separate, 5),

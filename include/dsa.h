@@ -60,7 +60,10 @@ typedef enum {
   DSA_ERR_BATCH = 5          /* dsa_check_batch(): cu_seqlens inconsistent with the sizes  */
 } dsa_status;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+/* Element types. DSA_FP8_E4M3 is OCP fp8 e4m3fn (1 byte; finite values up to 448, no infinity),
+ * accepted for the indexer inputs q_idx / k_idx only (dsa_indexer_scores_fp8, and dsa_forward
+ * with index_fp8 = 1). */
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
 
 /* Ragged batch description. Host integers plus two device arrays. */
 typedef struct {
@@ -88,6 +91,22 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
                               const float* w, int32_t index_n_heads, int32_t index_head_dim,
                               dsa_dtype dtype, float* scores, int64_t ld_scores,
                               hipStream_t stream);
+
+/* Step 1 with fp8 indexer inputs ("How GLM5.3 Sparse Attention Affects HBM Memory Usage",
+ * Evidence: the serving stacks run the decode path in FP8; "Sparse attention" glossary page,
+ * Why it matters: precision support decides the realised speed-up). q_idx and k_idx hold OCP
+ * e4m3fn bytes with the layouts above (index_head_dim = 128, index_n_heads 32 or 64); k_scale
+ * [total_k] fp32 is one non-negative scale per key row, or NULL for 1. The score is step 1's
+ * formula on the dequantised keys k_idx[s] * k_scale[s]:
+ *   scores[t * ld_scores + s] = k_scale[s] * sum_j w[t, j] * max(0, q_idx[t, j, :] . k_idx[s, :])
+ * (equal because max(0, c x) = c max(0, x) for c >= 0). Per-(token, head) query scales, if any,
+ * are non-negative factors of the same kind and go into w. Products are exact and accumulated in
+ * fp32, so integer-valued inputs with sums below 2^24 and power-of-two scales give exact scores.
+ * NaN bytes (0x7f, 0xff) in q_idx / k_idx give unspecified scores. */
+dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, const void* k_idx,
+                                  const float* k_scale, const float* w, int32_t index_n_heads,
+                                  int32_t index_head_dim, float* scores, int64_t ld_scores,
+                                  hipStream_t stream);
 
 /* Step 2 — causal top-k (same page and section: top-k 2048, dense below k).
  * For query t at position p: if p + 1 <= index_topk, indices[t] = 0, 1, .., p, then -1;
@@ -160,7 +179,9 @@ typedef struct {
   int32_t d_qk;
   int32_t d_v;
   float softmax_scale;
-  dsa_dtype dtype;
+  dsa_dtype dtype;               /* q, kv, out; and q_idx, k_idx unless index_fp8             */
+  int32_t index_fp8;             /* 1: q_idx, k_idx are fp8 e4m3fn (dsa_indexer_scores_fp8)     */
+  const float* k_idx_scale;      /* with index_fp8: [total_k] key scales, or NULL for 1        */
 } dsa_forward_args;
 
 /* Whole path with IndexShare (same page, How it works / IndexShare).

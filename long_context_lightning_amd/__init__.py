@@ -15,14 +15,15 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Batch", "indexer_scores", "topk", "sparse_mla_fwd", "sparse_mla_fwd_noalloc",
+__all__ = ["Batch", "indexer_scores", "indexer_scores_fp8", "topk", "sparse_mla_fwd", "sparse_mla_fwd_noalloc",
            "forward", "workspace_size",
            "check_batch", "lib", "LIB_PATH", "DsaError", "OP_INDEXER", "OP_TOPK",
            "OP_SPARSE_MLA", "OP_FORWARD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)   # OCP e4m3fn bytes
 OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
 
 _c = ctypes
@@ -47,7 +48,8 @@ class _CForwardArgs(_c.Structure):
     _fields_ = [("q_idx", _vp), ("k_idx", _vp), ("w", _vp), ("index_n_heads", _c.c_int32),
                 ("index_head_dim", _c.c_int32), ("index_topk", _c.c_int32), ("q", _vp),
                 ("kv", _vp), ("n_heads", _c.c_int32), ("d_qk", _c.c_int32),
-                ("d_v", _c.c_int32), ("softmax_scale", _c.c_float), ("dtype", _c.c_int)]
+                ("d_v", _c.c_int32), ("softmax_scale", _c.c_float), ("dtype", _c.c_int),
+                ("index_fp8", _c.c_int32), ("k_idx_scale", _vp)]
 
 
 _LIB = None
@@ -65,6 +67,9 @@ def _lib_handle():
         L.dsa_indexer_scores.argtypes = [B, _vp, _vp, _vp, _c.c_int32, _c.c_int32, _c.c_int, _vp,
                                          _c.c_int64, _vp]
         L.dsa_indexer_scores.restype = st
+        L.dsa_indexer_scores_fp8.argtypes = [B, _vp, _vp, _vp, _vp, _c.c_int32, _c.c_int32, _vp,
+                                             _c.c_int64, _vp]
+        L.dsa_indexer_scores_fp8.restype = st
         L.dsa_topk.argtypes = [B, _vp, _c.c_int64, _c.c_int32, _vp, _vp, _c.c_size_t, _vp]
         L.dsa_topk.restype = st
         L.dsa_sparse_mla_fwd.argtypes = [B, _vp, _vp, _vp, _c.c_int32, _c.c_int32, _c.c_int32,
@@ -193,6 +198,31 @@ def indexer_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, ba
     return out
 
 
+def indexer_scores_fp8(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, batch: Batch,
+                       k_scale: Optional[torch.Tensor] = None, ld: Optional[int] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Lightning-indexer scores from fp8 e4m3fn ``q_idx`` / ``k_idx`` (torch.float8_e4m3fn or
+    their uint8 bytes) with optional per-key scales ``k_scale`` [total_k] fp32."""
+    T = batch.total_q
+    _need(q_idx, "q_idx", (T, None, None))
+    if q_idx.dtype not in FP8_DTYPES or k_idx.dtype not in FP8_DTYPES:
+        raise ValueError("q_idx and k_idx must be float8_e4m3fn (or their uint8 bytes)")
+    H_I, d_I = q_idx.shape[1], q_idx.shape[2]
+    _need(k_idx, "k_idx", (batch.total_k, d_I))
+    _need(w, "w", (T, H_I), torch.float32)
+    if k_scale is not None:
+        _need(k_scale, "k_scale", (batch.total_k,), torch.float32)
+    ld = batch.max_seqlen_k if ld is None else int(ld)
+    if out is None:
+        out = torch.empty((T, ld), dtype=torch.float32, device=q_idx.device)
+    _need(out, "scores", (T, ld), torch.float32)
+    _check(_lib_handle().dsa_indexer_scores_fp8(
+        batch.ptr, q_idx.data_ptr(), k_idx.data_ptr(),
+        k_scale.data_ptr() if k_scale is not None else None, w.data_ptr(), H_I, d_I,
+        out.data_ptr(), ld, _stream(q_idx)), "dsa_indexer_scores_fp8")
+    return out
+
+
 def topk(scores: torch.Tensor, batch: Batch, index_topk: int,
          out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal top-k indices [T, index_topk] int32 (ascending, -1 padded)."""
@@ -256,12 +286,13 @@ def forward(q: torch.Tensor, kv: torch.Tensor, batch: Batch, index_topk: int,
             k_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
             shared_indices: Optional[torch.Tensor] = None, compute_indices: bool = True,
             out: Optional[torch.Tensor] = None, return_lse: bool = True,
-            workspace: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, k_idx_scale: Optional[torch.Tensor] = None):
     """Indexer -> top-k -> sparse MLA in one call.
 
     With ``compute_indices`` the indexer and top-k fill ``shared_indices`` (allocated if None);
     without it the cached ``shared_indices`` of an earlier layer of the IndexShare group are
-    reused. Returns (out, lse, shared_indices).
+    reused. fp8 (float8_e4m3fn) ``q_idx`` / ``k_idx`` select the fp8 indexer, with optional
+    per-key scales ``k_idx_scale``. Returns (out, lse, shared_indices).
     """
     T = batch.total_q
     _need(q, "q", (T, None, None))
@@ -273,11 +304,19 @@ def forward(q: torch.Tensor, kv: torch.Tensor, batch: Batch, index_topk: int,
         shared_indices = torch.empty((T, index_topk), dtype=torch.int32, device=q.device)
     _need(shared_indices, "shared_indices", (T, index_topk), torch.int32)
     H_I = d_I = 0
+    fp8 = False
     if compute_indices:
-        _need(q_idx, "q_idx", (T, None, None), q.dtype)
+        fp8 = q_idx is not None and q_idx.dtype in FP8_DTYPES
+        _need(q_idx, "q_idx", (T, None, None), None if fp8 else q.dtype)
         H_I, d_I = q_idx.shape[1], q_idx.shape[2]
-        _need(k_idx, "k_idx", (batch.total_k, d_I), q.dtype)
+        _need(k_idx, "k_idx", (batch.total_k, d_I), None if fp8 else q.dtype)
+        if fp8 and k_idx.dtype not in FP8_DTYPES:
+            raise ValueError("q_idx and k_idx must both be fp8")
         _need(w, "w", (T, H_I), torch.float32)
+        if k_idx_scale is not None:
+            if not fp8:
+                raise ValueError("k_idx_scale applies to fp8 indexer inputs only")
+            _need(k_idx_scale, "k_idx_scale", (batch.total_k,), torch.float32)
     if out is None:
         out = torch.empty((T, H, d_v), dtype=q.dtype, device=q.device)
     _need(out, "out", (T, H, d_v), q.dtype)
@@ -291,7 +330,8 @@ def forward(q: torch.Tensor, kv: torch.Tensor, batch: Batch, index_topk: int,
     args = _CForwardArgs(
         q_idx.data_ptr() if compute_indices else None, k_idx.data_ptr() if compute_indices else None,
         w.data_ptr() if compute_indices else None, H_I, d_I, index_topk, q.data_ptr(),
-        kv.data_ptr(), H, d_qk, d_v, float(softmax_scale), _dtype_code(q))
+        kv.data_ptr(), H, d_qk, d_v, float(softmax_scale), _dtype_code(q), 1 if fp8 else 0,
+        k_idx_scale.data_ptr() if (fp8 and k_idx_scale is not None) else None)
     _check(_lib_handle().dsa_forward(batch.ptr, _c.byref(args), shared_indices.data_ptr(),
                                      1 if compute_indices else 0, out.data_ptr(),
                                      lse.data_ptr() if lse is not None else None,

@@ -78,7 +78,7 @@ dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_id
                          int32_t hi, int32_t di, dsa_dtype dt, int64_t ld) {
   if (!batch_ok(b) || !q_idx || !k_idx || !w || hi <= 0 || di <= 0 || ld < b->max_seqlen_k)
     return DSA_ERR_INVALID_ARG;
-  if (dt == DSA_BF16) {
+  if (dt == DSA_BF16 || dt == DSA_FP8_E4M3) {
     if (di != 128 || (hi != 32 && hi != 64)) return DSA_ERR_UNSUPPORTED;
   } else if (dt == DSA_F32) {
     if (di > 256 || hi > 128) return DSA_ERR_UNSUPPORTED;
@@ -122,6 +122,7 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
                               dsa_dtype dtype, float* scores, int64_t ld_scores,
                               hipStream_t stream) {
   if (!scores) return DSA_ERR_INVALID_ARG;
+  if (dtype == DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;   // dsa_indexer_scores_fp8
   dsa_status st = check_indexer(batch, q_idx, k_idx, w, index_n_heads, index_head_dim, dtype,
                                 ld_scores);
   if (st != DSA_OK) return st;
@@ -133,6 +134,19 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
   return from_hip(dsa::launch_indexer_f32(b, (const float*)q_idx, (const float*)k_idx, w,
                                           index_n_heads, index_head_dim, scores, ld_scores,
                                           stream));
+}
+
+dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, const void* k_idx,
+                                  const float* k_scale, const float* w, int32_t index_n_heads,
+                                  int32_t index_head_dim, float* scores, int64_t ld_scores,
+                                  hipStream_t stream) {
+  if (!scores) return DSA_ERR_INVALID_ARG;
+  dsa_status st = check_indexer(batch, q_idx, k_idx, w, index_n_heads, index_head_dim,
+                                DSA_FP8_E4M3, ld_scores);
+  if (st != DSA_OK) return st;
+  if (batch->total_q == 0 || batch->total_k == 0) return DSA_OK;
+  return from_hip(dsa::launch_indexer_fp8(to_batch(batch), q_idx, k_idx, k_scale, w,
+                                          index_n_heads, scores, ld_scores, stream));
 }
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
@@ -219,8 +233,10 @@ size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_t* shared_indices,
                        int32_t compute_indices, void* out, float* lse, void* workspace,
                        size_t ws_bytes, hipStream_t stream) {
-  if (!a || !shared_indices || (compute_indices != 0 && compute_indices != 1))
+  if (!a || !shared_indices || (compute_indices != 0 && compute_indices != 1) ||
+      (a->index_fp8 != 0 && a->index_fp8 != 1))
     return DSA_ERR_INVALID_ARG;
+  const dsa_dtype idx_dt = a->index_fp8 ? DSA_FP8_E4M3 : a->dtype;
   dsa_status st = check_mla(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,
                             a->d_qk, a->d_v, a->softmax_scale, a->dtype, out);
   if (st != DSA_OK) return st;
@@ -235,13 +251,16 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
   const int64_t ld = batch->max_seqlen_k;
   if (compute_indices) {
     st = check_indexer(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads, a->index_head_dim,
-                       a->dtype, ld);
+                       idx_dt, ld);
     if (st != DSA_OK) return st;
   }
   if (batch->total_q == 0) return DSA_OK;
   if (compute_indices) {
-    st = dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
-                            a->index_head_dim, a->dtype, scores, ld, stream);
+    st = a->index_fp8
+             ? dsa_indexer_scores_fp8(batch, a->q_idx, a->k_idx, a->k_idx_scale, a->w,
+                                      a->index_n_heads, a->index_head_dim, scores, ld, stream)
+             : dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
+                                  a->index_head_dim, a->dtype, scores, ld, stream);
     if (st != DSA_OK) return st;
     st = dsa_topk(batch, scores, ld, a->index_topk, shared_indices, ws + s_bytes, t_bytes,
                   stream);
@@ -286,6 +305,6 @@ const char* dsa_status_string(dsa_status s) {
   return "unknown dsa_status";
 }
 
-int32_t dsa_version(void) { return 100; }
+int32_t dsa_version(void) { return 200; }
 
 }  // extern "C"

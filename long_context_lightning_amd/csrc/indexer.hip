@@ -145,6 +145,58 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
   }
 }
 
+// Boundaries of sequences lane, lane+64, .. as loaded by every lane of a wave for the lookup below.
+struct SeqBounds {
+  int64_t ka, kz;   // cu_k of the sequence and of the next one
+  int32_t qa, qz;   // cu_q likewise
+};
+
+__device__ __forceinline__ SeqBounds load_bounds(const int32_t* __restrict__ cu_q,
+                                                 const int64_t* __restrict__ cu_k, int nseq,
+                                                 int base) {
+  const int i = min(base + lane_id(), max(nseq - 1, 0));
+  SeqBounds r;
+  r.ka = cu_k[i];
+  r.kz = cu_k[i + 1];
+  r.qa = cu_q[i];
+  r.qz = cu_q[i + 1];
+  return r;
+}
+
+// The sequence holding flattened key row f: its key rows [kb0, kb1) and query rows [q0, q1).
+// One round trip per 64 sequences: lane i holds both boundaries of sequence base+i, a ballot over
+// cu_k finds the sequence and its boundaries come from that lane. `first` holds the boundaries of
+// sequences 0..63 when the caller loaded them earlier (PRELOADED).
+struct SeqSpan {
+  int64_t kb0, kb1;
+  int q0, q1;
+};
+
+template <bool PRELOADED>
+__device__ __forceinline__ SeqSpan seq_of_row(const int32_t* __restrict__ cu_q,
+                                              const int64_t* __restrict__ cu_k, int nseq,
+                                              int64_t f, const SeqBounds& first) {
+  const int lane = lane_id();
+  SeqSpan r{0, 0, 0, 0};
+  for (int base = 0;; base += WAVE) {
+    SeqBounds sb = (PRELOADED && base == 0) ? first : load_bounds(cu_q, cu_k, nseq, base);
+    asm volatile("" : "+v"(sb.ka), "+v"(sb.kz), "+v"(sb.qa), "+v"(sb.qz));
+    const bool le = base + lane + 1 < nseq && sb.kz <= f;
+    const int cnt = __popcll(__ballot(le));
+    if (cnt == WAVE) continue;
+    auto rd64 = [&](int64_t x) {
+      return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), cnt) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)x, cnt));
+    };
+    r.kb0 = rd64(sb.ka);
+    r.kb1 = rd64(sb.kz);
+    r.q0 = __builtin_amdgcn_readlane(sb.qa, cnt);
+    r.q1 = __builtin_amdgcn_readlane(sb.qz, cnt);
+    break;
+  }
+  return r;
+}
+
 // grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = query offset j within its sequence.
 template <int HB>
 __global__ __launch_bounds__(256) void indexer_decode_bf16(
@@ -164,9 +216,7 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   // the first three steps' key rows of this wave by flattened row (their addresses do not depend
   // on the lookup). Loads complete in issue order, so the lookup resolves without waiting for
   // the rows, and the query operands it selects are requested while the rows stream in.
-  const int i_first = min(lane, max(nseq - 1, 0));
-  int64_t ka_first = cu_k[i_first], kz_first = cu_k[i_first + 1];
-  int32_t qa_first = cu_q[i_first], qz_first = cu_q[i_first + 1];
+  const SeqBounds first = load_bounds(cu_q, cu_k, nseq, 0);
   __builtin_amdgcn_sched_barrier(0);           // keep them ahead of the rows
   bf16x8 b0[8], b1[8], b2[8];
   {
@@ -184,37 +234,10 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
   // One segment: the rows of the workgroup's range that belong to the sequence of row f.
   // Returns the first row past it, or f_end if the range cannot continue.
   auto segment = [&](auto preloaded) -> int64_t {
-    // one round trip: lane i loads both boundaries of sequence base+i from cu_k and cu_q, the
-    // ballot over cu_k finds the sequence of row f, its boundaries come from that lane
-    int64_t kb0 = 0, kb1 = 0;
-    int q0 = 0, q1 = 0;
-    for (int base = 0;; base += WAVE) {
-      int64_t ka, kz;
-      int32_t qa, qz;
-      if (decltype(preloaded)::value && base == 0) {   // loaded at the top of the kernel
-        ka = ka_first;
-        kz = kz_first;
-        qa = qa_first;
-        qz = qz_first;
-      } else {
-        const int i = min(base + lane, max(nseq - 1, 0));
-        ka = cu_k[i];
-        kz = cu_k[i + 1];
-        qa = cu_q[i];
-        qz = cu_q[i + 1];
-      }
-      asm volatile("" : "+v"(ka), "+v"(kz), "+v"(qa), "+v"(qz));
-      const bool le = base + lane + 1 < nseq && kz <= f;
-      const int cnt = __popcll(__ballot(le));
-      if (cnt == WAVE) continue;
-      kb0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(ka >> 32), cnt) << 32) |
-                      (uint32_t)__builtin_amdgcn_readlane((int)ka, cnt));
-      kb1 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kz >> 32), cnt) << 32) |
-                      (uint32_t)__builtin_amdgcn_readlane((int)kz, cnt));
-      q0 = __builtin_amdgcn_readlane(qa, cnt);
-      q1 = __builtin_amdgcn_readlane(qz, cnt);
-      break;
-    }
+    const SeqSpan sp = seq_of_row<decltype(preloaded)::value>(cu_q, cu_k, nseq, f, first);
+    const int64_t kb0 = sp.kb0;
+    int64_t kb1 = sp.kb1;
+    const int q0 = sp.q0, q1 = sp.q1;
     kb1 = min(kb1, total_k);
     if (kb1 <= f || kb0 > f) return f_end;
     const int64_t seg_end = min(f_end, kb1);
@@ -231,6 +254,153 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     return seg_end;
   };
   f = segment(std::true_type{});                 // usually the whole range
+  while (f < f_end) f = segment(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp8 (OCP e4m3fn) keys and queries, decode: the same work layout as the bf16 decode kernel with
+// 128-byte key rows. One 32x32x64 fp8 MFMA pairs byte e of lane half h of the A and B operands;
+// lane (key, h) holds bytes 64h .. 64h+63 of its key row as the operands of the two K steps and
+// lane (head, h) the same bytes of its query row, so each lane loads 64 contiguous bytes of its
+// row straight into the B layout (no LDS pass). With key scales, the head sum of a key is
+// multiplied by its scale (ReLU(s x) = s ReLU(x) for s >= 0).
+// ---------------------------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// one 32-key step of key rows as held by a lane: 64 bytes of its row and, with key scales, the
+// row's scale
+struct Fp8Rows {
+  u32x4 v[4];
+  float sc;
+};
+
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int HB, bool SCALED>
+__device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q_idx,
+                                                   const uint8_t* __restrict__ k_idx,
+                                                   const float* __restrict__ k_scale,
+                                                   const float* __restrict__ w, int t,
+                                                   int64_t kb0, int64_t s_beg, int64_t s_end,
+                                                   float* __restrict__ srow, int stride,
+                                                   bool preloaded, Fp8Rows& b0, Fp8Rows& b1,
+                                                   Fp8Rows& b2) {
+  constexpr int HI = 32 * HB;
+  auto uni = [](int64_t x) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)x));
+  };
+  s_beg = uni(s_beg);
+  s_end = uni(s_end);
+  kb0 = uni(kb0);
+  t = __builtin_amdgcn_readfirstlane(t);
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  i32x8 a[HB][2];
+  float wr[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const uint8_t* qr = q_idx + ((int64_t)t * HI + hb * 32 + col) * D + 64 * half;
+    a[hb][0] = *(const i32x8*)qr;
+    a[hb][1] = *(const i32x8*)(qr + 32);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[hb][r] = w[(int64_t)t * HI + hb * 32 + mfma32_row(r, lane)];
+  }
+  const uint8_t* kb = k_idx + kb0 * D + 64 * half;
+  auto load = [&](int64_t s0, Fp8Rows& dst) {
+    const int64_t s = min(s0 + col, s_end - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst.v[i] = *(const u32x4*)(kb + s * D + 16 * i);
+    if constexpr (SCALED) dst.sc = k_scale[kb0 + s];
+  };
+  auto step = [&](int64_t s0, const Fp8Rows& rows) {
+    const i32x8 k0 = cat8(rows.v[0], rows.v[1]), k1 = cat8(rows.v[2], rows.v[3]);
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x16 acc = mfma32x32x64_fp8(a[hb][0], k0, f32x16{});
+      acc = mfma32x32x64_fp8(a[hb][1], k1, acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], relu(acc[r]), v);
+    }
+    v = halves_sum(v);
+    if constexpr (SCALED) v *= rows.sc;
+    const int64_t s = s0 + col;
+    if (half == 0 && s < s_end) srow[s] = v;
+  };
+  if (s_beg >= s_end) return;
+  if (!preloaded) {
+    load(s_beg, b0);
+    load(min(s_beg + stride, s_end - 1), b1);
+    load(min(s_beg + 2 * stride, s_end - 1), b2);
+  }
+#pragma unroll
+  for (int i = 0; i < DEC_NSTEP; ++i) {
+    const int64_t s0 = s_beg + (int64_t)i * stride;
+    if (s0 >= s_end) break;                      // uniform
+    Fp8Rows& cur = i % 3 == 0 ? b0 : (i % 3 == 1 ? b1 : b2);
+    step(s0, cur);
+    if (i + 3 < DEC_NSTEP) load(min(s0 + 3 * stride, s_end - 1), cur);
+  }
+}
+
+// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = query offset j within its sequence.
+template <int HB, bool SCALED>
+__global__ __launch_bounds__(256) void indexer_decode_fp8(
+    const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const float* __restrict__ w,
+    const int32_t* __restrict__ cu_q, const int64_t* __restrict__ cu_k, int nseq, int total_q,
+    int64_t total_k, float* __restrict__ scores, int64_t ld) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int j = blockIdx.y;
+  int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
+  const int64_t f_end = min(f + DEC_KEYS_PER_BLOCK, total_k);
+  // as in the bf16 kernel: the lookup's loads first, then the first three steps' key rows by
+  // flattened row
+  const SeqBounds first = load_bounds(cu_q, cu_k, nseq, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  Fp8Rows b0, b1, b2;
+  {
+    const uint8_t* kr = k_idx + 64 * (lane >> 5);
+    auto pre = [&](int64_t r, Fp8Rows& dst) {
+      r = min(r, total_k - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst.v[i] = *(const u32x4*)(kr + r * D + 16 * i);
+      if constexpr (SCALED) dst.sc = k_scale[r];
+    };
+    const int64_t r0 = f + DEC_STEP * wave + (lane & 31);
+    pre(r0, b0);
+    pre(r0 + DEC_STEP * DEC_WAVES, b1);
+    pre(r0 + 2 * DEC_STEP * DEC_WAVES, b2);
+  }
+  auto segment = [&](auto preloaded) -> int64_t {
+    const SeqSpan sp = seq_of_row<decltype(preloaded)::value>(cu_q, cu_k, nseq, f, first);
+    const int64_t kb0 = sp.kb0;
+    const int64_t kb1 = min(sp.kb1, total_k);
+    if (kb1 <= f || kb0 > f) return f_end;
+    const int64_t seg_end = min(f_end, kb1);
+    const int nq = sp.q1 - sp.q0;
+    if (j < nq && sp.q0 + j < total_q && sp.q0 + j >= 0) {
+      const int t = sp.q0 + j;
+      const int64_t p = (kb1 - kb0) - nq + j;
+      const int64_t s_beg = f - kb0;
+      const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
+      decode_segment_fp8<HB, SCALED>(q_idx, k_idx, k_scale, w, t, kb0, s_beg + DEC_STEP * wave,
+                                     s_end, scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES,
+                                     decltype(preloaded)::value, b0, b1, b2);
+    }
+    return seg_end;
+  };
+  f = segment(std::true_type{});
   while (f < f_end) f = segment(std::false_type{});
 }
 
@@ -512,6 +682,23 @@ hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_
       indexer_decode_bf16<2><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
                                                        b.total_q, b.total_k, scores, ld);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_idx,
+                              const float* k_scale, const float* w, int index_n_heads,
+                              float* scores, int64_t ld, hipStream_t stream) {
+  const uint8_t* q = (const uint8_t*)q_idx;
+  const uint8_t* k = (const uint8_t*)k_idx;
+  dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK), b.max_q);
+  auto go = [&](auto kern) {
+    kern<<<grid, 256, 0, stream>>>(q, k, k_scale, w, b.cu_q, b.cu_k, b.nseq, b.total_q,
+                                   b.total_k, scores, ld);
+  };
+  if (index_n_heads == 32)
+    k_scale ? go(indexer_decode_fp8<1, true>) : go(indexer_decode_fp8<1, false>);
+  else
+    k_scale ? go(indexer_decode_fp8<2, true>) : go(indexer_decode_fp8<2, false>);
   return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@ struct Batch {
 hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_idx,
                                const float* w, int index_n_heads, float* scores, int64_t ld,
                                hipStream_t stream);
+// fp8 (e4m3fn) queries and keys; k_scale [total_k] or null.
+hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_idx,
+                              const float* k_scale, const float* w, int index_n_heads,
+                              float* scores, int64_t ld, hipStream_t stream);
 hipError_t launch_indexer_f32(const Batch& b, const float* q_idx, const float* k_idx,
                               const float* w, int index_n_heads, int index_head_dim,
                               float* scores, int64_t ld, hipStream_t stream);

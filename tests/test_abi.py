@@ -145,3 +145,20 @@ def test_sparse_mla_noalloc_rejects_bad_arguments(L):
     a = list(args); a[8] = float("nan")
     assert f(*a) == INVALID
     assert f(None, *args[1:]) == INVALID
+
+
+def test_fp8_indexer_rejects_bad_arguments(L):
+    b = _batch()
+    assert L.dsa_indexer_scores(ctypes.byref(b), FAKE, FAKE, FAKE, 32, 128, 2, FAKE, 60,
+                                None) == UNSUPPORTED          # fp8 goes through the _fp8 call
+    f = L.dsa_indexer_scores_fp8
+    assert f(ctypes.byref(b), None, FAKE, None, FAKE, 32, 128, FAKE, 60, None) == INVALID
+    assert f(ctypes.byref(b), FAKE, FAKE, None, None, 32, 128, FAKE, 60, None) == INVALID
+    assert f(ctypes.byref(b), FAKE, FAKE, None, FAKE, 32, 128, None, 60, None) == INVALID
+    assert f(ctypes.byref(b), FAKE, FAKE, None, FAKE, 32, 128, FAKE, 59, None) == INVALID
+    assert f(ctypes.byref(b), FAKE, FAKE, None, FAKE, 48, 128, FAKE, 60, None) == UNSUPPORTED
+    assert f(ctypes.byref(b), FAKE, FAKE, None, FAKE, 32, 64, FAKE, 60, None) == UNSUPPORTED
+    fa = _CForwardArgs(FAKE, FAKE, FAKE, 32, 128, 2048, FAKE, FAKE, 64, 576, 512, 1 / 24, 1, 2,
+                       None)                                   # index_fp8 must be 0 or 1
+    assert L.dsa_forward(ctypes.byref(b), ctypes.byref(fa), FAKE, 1, FAKE, None, FAKE, 1 << 30,
+                         None) == INVALID
