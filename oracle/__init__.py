@@ -15,7 +15,8 @@ what the path computes, written from the pages' description of DeepSeek Sparse A
   indices are reused by the shared layers.
 * "DeepSeek Sparse Attention" technique page, table "In the code": the indexer is a weighted
   sum of ReLU(q.k) and queries attend only to the top index_topk tokens (the selection can be
-  written as an additive sparse mask over dense attention).
+  written as an additive sparse mask over dense attention); one variant pools the scores into
+  blocks and keeps the top blocks (block_topk_row).
 
 Every function states which of these it follows. Pins that tie the oracle to something other
 than itself live in ``tests/test_oracle_pins.py``; the functions with no pin are listed there
@@ -27,6 +28,8 @@ from .dsa_oracle import (  # noqa: F401
     indexer_scores,
     topk_row,
     topk,
+    pool_blocks_row,
+    block_topk_row,
     sparse_attention_row,
     sparse_attention,
     dense_masked_attention_row,

@@ -88,6 +88,49 @@ def topk(score_rows, k):
 
 
 # ---------------------------------------------------------------------------------------------
+# Step 2, block-pooled variant.
+# "DeepSeek Sparse Attention" technique page, In the code: MiniMax-M3's lightning indexer pools
+# its scores into blocks and keeps the top index_topk_blocks blocks per query; GLM-5.3-Flash's
+# indexer scores pooled candidates. Reading taken: the visible scores of a query (positions
+# 0..p) are cut into blocks of `block` consecutive positions (the last block holds the remainder);
+# a block's score is the maximum, or the mean, of its visible scores; the k_blocks best blocks are
+# chosen with the token-level rule (higher score first, an equal score going to the lower block,
+# every block when at most k_blocks are visible); the query then attends to every visible position
+# of the chosen blocks, emitted ascending and padded with -1 to k_blocks * block.
+# A mean is a float64 quotient rounded once to fp32 before the blocks are compared: the selection
+# is decided in the precision the kernel compares in (for integer-valued scores whose block sums
+# stay below 2^24 the kernel's fp32 sum is exact and its fp32 quotient is that same rounding).
+# ---------------------------------------------------------------------------------------------
+def pool_blocks_row(scores, block, pool):
+    """Block scores of one causal score row: float64 [ceil(n / block)]."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    nb = (n + block - 1) // block
+    out = np.empty(nb)
+    for c in range(nb):
+        seg = s[c * block:min(n, (c + 1) * block)]
+        if pool == "max":
+            out[c] = seg.max()
+        elif pool == "mean":
+            out[c] = np.float64(np.float32(seg.sum() / seg.shape[0]))
+        else:
+            raise ValueError(pool)
+    return out
+
+
+def block_topk_row(scores, block, k_blocks, pool):
+    """Positions attended by one query under block-pooled selection: int64 [k_blocks * block]."""
+    n = np.asarray(scores).shape[0]
+    chosen = topk_row(pool_blocks_row(scores, block, pool), k_blocks)
+    out = np.full(k_blocks * block, -1, dtype=np.int64)
+    pos = [np.arange(c * block, min(n, (c + 1) * block)) for c in chosen if c >= 0]
+    if pos:
+        pos = np.concatenate(pos)
+        out[:pos.shape[0]] = pos
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
 # Step 3: sparse MLA in MQA mode.
 # "How GLM5.3 ...", How it works / Model: all query heads attend, with softmax, over only the
 # selected latent rows; the key of a row is its full latent+rope vector and (weight absorption)

@@ -239,6 +239,74 @@ def pin_attention_invariants():
     assert np.allclose(lse, np.log(np.exp(z).sum(axis=1)), rtol=1e-12)
 
 
+# ------------------------------------------------------------------ block-pooled selection pins
+def pin_block_topk_worked():
+    g = _load("block_topk_worked.json")
+    for c in g["cases"]:
+        s = np.array([_f(x) for x in c["scores"]])
+        for pool in ("max", "mean"):
+            got = O.block_topk_row(s, c["block"], c["k"], pool)
+            assert got.tolist() == c[pool], (c["why"], pool, got.tolist())
+
+
+def pin_block_topk_block1_is_token_topk():
+    # blocks of one position: every pooling is the score itself, so the selection is top-k
+    rng = np.random.default_rng(31)
+    for _ in range(60):
+        n = int(rng.integers(1, 200))
+        s = rng.integers(-4, 5, n).astype(np.float64)
+        k = int(rng.integers(1, 40))
+        want = O.topk_row(s, k)
+        for pool in ("max", "mean"):
+            assert np.array_equal(O.block_topk_row(s, 1, k, pool), want), (n, k, pool)
+
+
+def pin_block_topk_brute_force():
+    # block c is chosen iff fewer than k blocks beat it (a higher pooled score, or an equal one
+    # at a lower block), or every block is chosen when at most k are visible; the output is the
+    # chosen blocks' visible positions, ascending
+    rng = np.random.default_rng(37)
+    for _ in range(200):
+        n = int(rng.integers(1, 300))
+        block = int(rng.choice([2, 3, 4, 8, 16]))
+        k = int(rng.integers(1, 12))
+        s = rng.integers(-3, 4, n).astype(np.float64)
+        for pool in ("max", "mean"):
+            J = O.pool_blocks_row(s, block, pool)
+            nb = J.shape[0]
+            chosen = [c for c in range(nb)
+                      if nb <= k or sum(1 for d in range(nb)
+                                        if J[d] > J[c] or (J[d] == J[c] and d < c)) < k]
+            want = [x for c in chosen for x in range(c * block, min(n, (c + 1) * block))]
+            got = O.block_topk_row(s, block, k, pool)
+            assert got[:len(want)].tolist() == want and (got[len(want):] == -1).all(), \
+                (n, block, k, pool)
+            assert got.shape == (k * block,)
+
+
+def pin_block_topk_invariants():
+    rng = np.random.default_rng(41)
+    for _ in range(100):
+        n = int(rng.integers(2, 400))
+        block = int(rng.choice([4, 8, 16, 64]))
+        k = int(rng.integers(1, 8))
+        s = rng.integers(-6, 7, n).astype(np.float64)
+        for pool in ("max", "mean"):
+            base = O.block_topk_row(s, block, k, pool)
+            # the pooled score of a block does not depend on the order inside it
+            p = s.copy()
+            for c in range(0, n, block):
+                seg = p[c:c + block]
+                p[c:c + block] = seg[rng.permutation(seg.shape[0])]
+            assert np.array_equal(O.block_topk_row(p, block, k, pool), base)
+            # nor on a constant added to every score
+            assert np.array_equal(O.block_topk_row(s + 5.0, block, k, pool), base)
+        # max pooling always keeps the block of the best-scoring position
+        top = int(np.argmax(s)) // block
+        chosen = set(x // block for x in O.block_topk_row(s, block, k, "max") if x >= 0)
+        assert top in chosen
+
+
 # --------------------------------------------------------------------------- IndexShare pin
 def pin_index_share():
     rng = np.random.default_rng(41)
@@ -285,7 +353,9 @@ def pin_index_share():
 ALL_PINS = [pin_indexer_worked, pin_indexer_one_hot_closed_form, pin_indexer_relu_identity,
             pin_indexer_invariants, pin_topk_worked, pin_topk_brute_force,
             pin_topk_special_cases, pin_attention_worked, pin_attention_dense_equals_sdpa,
-            pin_attention_mask_form, pin_attention_invariants, pin_index_share]
+            pin_attention_mask_form, pin_attention_invariants, pin_index_share,
+            pin_block_topk_worked, pin_block_topk_block1_is_token_topk,
+            pin_block_topk_brute_force, pin_block_topk_invariants]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -372,6 +442,46 @@ def _m_positions_wrong_base(cu_q, cu_k):
     return out
 
 
+def _m_pool_shifted_boundaries(scores, block, pool):
+    s = np.asarray(scores, float)
+    n = s.shape[0]
+    nb = (n + block - 1) // block
+    out = np.empty(nb)
+    for c in range(nb):                                # blocks start one position late
+        seg = s[min(n - 1, c * block + 1):min(n, (c + 1) * block + 1)]
+        out[c] = seg.max() if pool == "max" else seg.mean()
+    return out
+
+
+def _m_pool_mean_over_whole_block(scores, block, pool):
+    s = np.asarray(scores, float)
+    n = s.shape[0]
+    nb = (n + block - 1) // block
+    out = np.empty(nb)
+    for c in range(nb):                                # the last block divides by `block`
+        seg = s[c * block:min(n, (c + 1) * block)]
+        out[c] = seg.max() if pool == "max" else seg.sum() / block
+    return out
+
+
+def _m_pool_ignores_kind(scores, block, pool):
+    s = np.asarray(scores, float)
+    n = s.shape[0]
+    return np.array([s[c:min(n, c + block)].mean() for c in range(0, n, block)])
+
+
+def _m_block_drops_partial_block(scores, block, k_blocks, pool):
+    n = np.asarray(scores).shape[0]
+    chosen = O.topk_row(O.pool_blocks_row(scores, block, pool), k_blocks)
+    out = np.full(k_blocks * block, -1, dtype=np.int64)
+    pos = [np.arange(c * block, (c + 1) * block) for c in chosen
+           if c >= 0 and (c + 1) * block <= n]         # forgets the remainder block
+    if pos:
+        pos = np.concatenate(pos)
+        out[:pos.shape[0]] = pos
+    return out
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores_row", _m_no_relu),
     "indexer_relu_after_weight": ("indexer_scores_row", _m_relu_after_weight),
@@ -385,6 +495,10 @@ MUTANTS = {
     "attention_lse_without_max": ("sparse_attention_row", _attn_variant(lse_without_max=True)),
     "causal_excludes_self": ("query_positions", _m_positions_exclusive),
     "ragged_base_ignored": ("query_positions", _m_positions_wrong_base),
+    "block_boundaries_shifted": ("pool_blocks_row", _m_pool_shifted_boundaries),
+    "block_mean_divides_by_block": ("pool_blocks_row", _m_pool_mean_over_whole_block),
+    "block_pool_always_mean": ("pool_blocks_row", _m_pool_ignores_kind),
+    "block_remainder_dropped": ("block_topk_row", _m_block_drops_partial_block),
 }
 
 
