@@ -37,6 +37,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b32_l16k")
+    ap.add_argument("--select", choices=["token", "block"], default="token",
+                    help="per-position top-k (default) or block-pooled selection of "
+                         "index_topk / block-size blocks")
+    ap.add_argument("--block-size", type=int, default=64)
+    ap.add_argument("--pool", choices=["max", "mean"], default="max")
     ap.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="element type of the indexer inputs q_I / k_I (fp8: OCP e4m3fn; the "
                          "attention stays bf16)")
@@ -236,6 +241,11 @@ def main():
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
     tws_n = dsa.workspace_size(dsa.OP_TOPK, batch, case.index_topk)
     tws = torch.empty(max(tws_n, 1), dtype=torch.uint8, device="cuda")
+    blk = args.select == "block"
+    pool_code = 1 if args.pool == "mean" else 0
+    if blk:
+        tws_n = int(dsa.lib().dsa_block_topk_workspace_size(batch.ptr, args.block_size))
+        tws = torch.empty(max(tws_n, 1), dtype=torch.uint8, device="cuda")
     fws_n = dsa.workspace_size(dsa.OP_FORWARD, batch, case.index_topk, case.n_heads, case.d_v)
     fws = torch.empty(max(fws_n, 1), dtype=torch.uint8, device="cuda")
     L = dsa.lib()
@@ -246,7 +256,7 @@ def main():
                                 case.index_n_heads, case.index_head_dim, case.index_topk,
                                 d["q"][l].data_ptr(), d["kv"][l].data_ptr(), case.n_heads,
                                 case.d_qk, case.d_v, case.softmax_scale, 1, 1 if fp8 else 0,
-                                None)
+                                None, args.block_size if blk else 0, pool_code)
               for l in range(case.layers)] for d in sets]
 
     def fused_on(i, sp):
@@ -279,8 +289,13 @@ def main():
         st = idx_on(d, sp)
         if ev is not None:
             ev[1].record(stream)
-        st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
-                         tws.data_ptr(), tws.numel(), sp)
+        if blk:
+            st |= L.dsa_block_topk(batch.ptr, scores.data_ptr(), ld, args.block_size, pool_code,
+                                   case.index_topk // args.block_size, idx.data_ptr(),
+                                   tws.data_ptr(), tws.numel(), sp)
+        else:
+            st |= L.dsa_topk(batch.ptr, scores.data_ptr(), ld, case.index_topk, idx.data_ptr(),
+                             tws.data_ptr(), tws.numel(), sp)
         if ev is not None:
             ev[2].record(stream)
         for l in range(case.layers):       # IndexShare: the group's layers reuse the indices
@@ -451,6 +466,9 @@ def main():
                                f"({case.d_v} value), {case.layers} layer(s) per index pass",
                    "batch": case.batch, "query_tokens": T, "input_sets_rotated": nsets,
                    "indexer_inputs": "fp8 e4m3fn" if fp8 else case.dtype.__str__()[6:],
+                   "selection": (f"block-pooled ({args.pool}): top-{case.index_topk // args.block_size}"
+                                 f" blocks of {args.block_size}") if blk else
+                                f"per-position top-{case.index_topk}",
                    "launch": "hip_graph" if args.launch == "graph" else "eager"},
         "eager_ms_per_step": round(ms_eager, 5),
         "separate_calls_ms_per_step": round(ms_separate, 5),

@@ -124,6 +124,30 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
                     int32_t index_topk, int32_t* indices, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Step 2, block-pooled variant ("DeepSeek Sparse Attention" technique page, In the code:
+ * MiniMax-M3 pools its indexer scores into blocks and keeps the top index_topk_blocks blocks per
+ * query; GLM-5.3-Flash scores pooled candidates).
+ * For query t at position p, positions 0..p are cut into blocks of block_size consecutive
+ * positions (the last block holds the remainder). A block's score is the maximum (DSA_POOL_MAX)
+ * or the mean over its visible positions (DSA_POOL_MEAN, an fp32 quotient) of its scores. The
+ * topk_blocks best blocks are chosen as step 2 chooses positions (scores compare as reals, an
+ * equal score goes to the lower block; every block when at most topk_blocks are visible), and
+ * indices[t] lists every visible position of the chosen blocks, ascending, padded with -1:
+ *   scores  [T, ld_scores] fp32 (only s <= p is read; must not be NaN)
+ *   indices [T, topk_blocks * block_size] int32, sequence-local positions; pass
+ *           index_topk = topk_blocks * block_size to the sparse-MLA call that reads them.
+ * block_size is a power of two in 4..256, 1 <= topk_blocks <= 1024, and max_seqlen_k /
+ * block_size (rounded up) at most 32768; otherwise DSA_ERR_UNSUPPORTED.
+ * workspace: dsa_block_topk_workspace_size() bytes (the block scores); contents on entry do not
+ * matter, on return they are undefined. Mean pooling sums in fp32: for integer-valued scores
+ * whose block sums stay below 2^24 the block scores are exact quotients. */
+typedef enum { DSA_POOL_MAX = 0, DSA_POOL_MEAN = 1 } dsa_pool;
+dsa_status dsa_block_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
+                          int32_t block_size, dsa_pool pool, int32_t topk_blocks,
+                          int32_t* indices, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+size_t dsa_block_topk_workspace_size(const dsa_batch* batch, int32_t block_size);
+
 /* Step 3 — sparse MLA forward in MQA mode (same page and section).
  *   z_s = softmax_scale * sum_{c < d_qk} q[t, h, c] * kv[cu_k[b] + s, c]   for s in indices[t]
  *   out[t, h, :] = sum_s softmax(z)_s * kv[cu_k[b] + s, 0:d_v];  lse[t, h] = ln sum_s exp(z_s)
@@ -182,6 +206,9 @@ typedef struct {
   dsa_dtype dtype;               /* q, kv, out; and q_idx, k_idx unless index_fp8             */
   int32_t index_fp8;             /* 1: q_idx, k_idx are fp8 e4m3fn (dsa_indexer_scores_fp8)     */
   const float* k_idx_scale;      /* with index_fp8: [total_k] key scales, or NULL for 1        */
+  int32_t block_size;            /* 0: step 2 per position; else block-pooled selection        */
+                                 /* (dsa_block_topk) of index_topk / block_size blocks          */
+  int32_t pool;                  /* with block_size: DSA_POOL_MAX or DSA_POOL_MEAN             */
 } dsa_forward_args;
 
 /* Whole path with IndexShare (same page, How it works / IndexShare).
@@ -189,8 +216,9 @@ typedef struct {
  *                      reads them (q_idx, k_idx, w must be valid).
  * compute_indices = 0: shared_indices is read as cached by an earlier call of the group;
  *                      q_idx / k_idx / w are ignored and may be NULL.
- * The workspace holds the [T, max_seqlen_k] fp32 score matrix plus the top-k and split-KV
- * scratch: dsa_workspace_size(DSA_OP_FORWARD, ...) bytes. */
+ * With block_size > 0 the selection is dsa_block_topk's (index_topk a multiple of block_size).
+ * The workspace holds the [T, max_seqlen_k] fp32 score matrix plus the selection and split-KV
+ * scratch: dsa_workspace_size(DSA_OP_FORWARD, ...) bytes (enough for either selection). */
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* args,
                        int32_t* shared_indices, int32_t compute_indices, void* out, float* lse,
                        void* workspace, size_t ws_bytes, hipStream_t stream);

@@ -15,7 +15,7 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Batch", "indexer_scores", "indexer_scores_fp8", "topk", "sparse_mla_fwd", "sparse_mla_fwd_noalloc",
+__all__ = ["Batch", "indexer_scores", "indexer_scores_fp8", "topk", "block_topk", "sparse_mla_fwd", "sparse_mla_fwd_noalloc",
            "forward", "workspace_size",
            "check_batch", "lib", "LIB_PATH", "DsaError", "OP_INDEXER", "OP_TOPK",
            "OP_SPARSE_MLA", "OP_FORWARD"]
@@ -49,7 +49,8 @@ class _CForwardArgs(_c.Structure):
                 ("index_head_dim", _c.c_int32), ("index_topk", _c.c_int32), ("q", _vp),
                 ("kv", _vp), ("n_heads", _c.c_int32), ("d_qk", _c.c_int32),
                 ("d_v", _c.c_int32), ("softmax_scale", _c.c_float), ("dtype", _c.c_int),
-                ("index_fp8", _c.c_int32), ("k_idx_scale", _vp)]
+                ("index_fp8", _c.c_int32), ("k_idx_scale", _vp), ("block_size", _c.c_int32),
+                ("pool", _c.c_int32)]
 
 
 _LIB = None
@@ -72,6 +73,11 @@ def _lib_handle():
         L.dsa_indexer_scores_fp8.restype = st
         L.dsa_topk.argtypes = [B, _vp, _c.c_int64, _c.c_int32, _vp, _vp, _c.c_size_t, _vp]
         L.dsa_topk.restype = st
+        L.dsa_block_topk.argtypes = [B, _vp, _c.c_int64, _c.c_int32, _c.c_int, _c.c_int32, _vp,
+                                     _vp, _c.c_size_t, _vp]
+        L.dsa_block_topk.restype = st
+        L.dsa_block_topk_workspace_size.argtypes = [B, _c.c_int32]
+        L.dsa_block_topk_workspace_size.restype = _c.c_size_t
         L.dsa_sparse_mla_fwd.argtypes = [B, _vp, _vp, _vp, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int32, _c.c_float, _c.c_int, _vp, _vp, _vp,
                                          _c.c_size_t, _vp]
@@ -238,6 +244,32 @@ def topk(scores: torch.Tensor, batch: Batch, index_topk: int,
     return out
 
 
+POOL_MAX, POOL_MEAN = 0, 1
+
+
+def block_topk(scores: torch.Tensor, batch: Batch, block_size: int, topk_blocks: int,
+               pool: str = "max", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-pooled selection: every visible position of the ``topk_blocks`` best blocks of
+    ``block_size`` positions (block score = max or mean of its scores), [T, topk_blocks *
+    block_size] int32, ascending, -1 padded."""
+    T = batch.total_q
+    _need(scores, "scores", (T, None), torch.float32)
+    if pool not in ("max", "mean"):
+        raise ValueError("pool must be 'max' or 'mean'")
+    n = topk_blocks * block_size
+    if out is None:
+        out = torch.empty((T, n), dtype=torch.int32, device=scores.device)
+    _need(out, "indices", (T, n), torch.int32)
+    L = _lib_handle()
+    nb = int(L.dsa_block_topk_workspace_size(batch.ptr, block_size))
+    ws, nb = _workspace(nb, scores.device)
+    _check(L.dsa_block_topk(batch.ptr, scores.data_ptr(), scores.shape[1], block_size,
+                            POOL_MEAN if pool == "mean" else POOL_MAX, topk_blocks,
+                            out.data_ptr(), ws.data_ptr() if ws is not None else None, nb,
+                            _stream(scores)), "dsa_block_topk")
+    return out
+
+
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, batch: Batch,
                    softmax_scale: float, d_v: int, out: Optional[torch.Tensor] = None,
                    return_lse: bool = True):
@@ -286,13 +318,16 @@ def forward(q: torch.Tensor, kv: torch.Tensor, batch: Batch, index_topk: int,
             k_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
             shared_indices: Optional[torch.Tensor] = None, compute_indices: bool = True,
             out: Optional[torch.Tensor] = None, return_lse: bool = True,
-            workspace: Optional[torch.Tensor] = None, k_idx_scale: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, k_idx_scale: Optional[torch.Tensor] = None,
+            block_size: int = 0, pool: str = "max"):
     """Indexer -> top-k -> sparse MLA in one call.
 
     With ``compute_indices`` the indexer and top-k fill ``shared_indices`` (allocated if None);
     without it the cached ``shared_indices`` of an earlier layer of the IndexShare group are
     reused. fp8 (float8_e4m3fn) ``q_idx`` / ``k_idx`` select the fp8 indexer, with optional
-    per-key scales ``k_idx_scale``. Returns (out, lse, shared_indices).
+    per-key scales ``k_idx_scale``. ``block_size`` > 0 selects whole blocks (dsa_block_topk:
+    index_topk / block_size blocks, ``pool`` 'max' or 'mean'). Returns (out, lse,
+    shared_indices).
     """
     T = batch.total_q
     _need(q, "q", (T, None, None))
@@ -331,7 +366,8 @@ def forward(q: torch.Tensor, kv: torch.Tensor, batch: Batch, index_topk: int,
         q_idx.data_ptr() if compute_indices else None, k_idx.data_ptr() if compute_indices else None,
         w.data_ptr() if compute_indices else None, H_I, d_I, index_topk, q.data_ptr(),
         kv.data_ptr(), H, d_qk, d_v, float(softmax_scale), _dtype_code(q), 1 if fp8 else 0,
-        k_idx_scale.data_ptr() if (fp8 and k_idx_scale is not None) else None)
+        k_idx_scale.data_ptr() if (fp8 and k_idx_scale is not None) else None, int(block_size),
+        POOL_MEAN if pool == "mean" else POOL_MAX)
     _check(_lib_handle().dsa_forward(batch.ptr, _c.byref(args), shared_indices.data_ptr(),
                                      1 if compute_indices else 0, out.data_ptr(),
                                      lse.data_ptr() if lse is not None else None,

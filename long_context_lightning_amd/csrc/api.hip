@@ -1,5 +1,6 @@
 // C ABI of libdsa: host-side validation, workspace layout and launch sequencing.
 // Every check runs before anything is enqueued; calls only enqueue work on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -113,6 +114,12 @@ size_t scores_bytes(const dsa_batch* b) {
   return align_up((size_t)b->total_q * (size_t)b->max_seqlen_k * sizeof(float));
 }
 
+// Selection scratch of the fused call: enough for the per-position top-k and for the block
+// selection of any block size (the smallest, 4, needs the most).
+size_t select_bytes(const Batch& b, int32_t k) {
+  return align_up(std::max(dsa::topk_workspace_bytes(b, k), dsa::block_topk_workspace_bytes(b, 4)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +167,27 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
   if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (batch->total_q == 0) return DSA_OK;
   return from_hip(dsa::launch_topk(b, scores, ld_scores, index_topk, indices, workspace, stream));
+}
+
+dsa_status dsa_block_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
+                          int32_t block_size, dsa_pool pool, int32_t topk_blocks,
+                          int32_t* indices, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!batch_ok(batch) || !scores || !indices || topk_blocks <= 0 || block_size <= 0 ||
+      ld_scores < batch->max_seqlen_k || (pool != DSA_POOL_MAX && pool != DSA_POOL_MEAN))
+    return DSA_ERR_INVALID_ARG;
+  const Batch b = to_batch(batch);
+  if (!dsa::block_topk_supported(b, block_size, topk_blocks)) return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa::block_topk_workspace_bytes(b, block_size);
+  if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (batch->total_q == 0) return DSA_OK;
+  return from_hip(dsa::launch_block_topk(b, scores, ld_scores, block_size, pool == DSA_POOL_MEAN,
+                                         topk_blocks, indices, workspace, stream));
+}
+
+size_t dsa_block_topk_workspace_size(const dsa_batch* batch, int32_t block_size) {
+  if (!batch_ok(batch) || block_size <= 0) return 0;
+  return dsa::block_topk_workspace_bytes(to_batch(batch), block_size);
 }
 
 dsa_status dsa_sparse_mla_fwd(const dsa_batch* batch, const void* q, const void* kv,
@@ -224,8 +252,7 @@ size_t dsa_workspace_size(dsa_op op, const dsa_batch* batch, int32_t index_topk,
     case DSA_OP_SPARSE_MLA:
       return mla;
     case DSA_OP_FORWARD:
-      return scores_bytes(batch) + align_up(dsa::topk_workspace_bytes(b, index_topk)) +
-             align_up(mla);
+      return scores_bytes(batch) + select_bytes(b, index_topk) + align_up(mla);
   }
   return 0;
 }
@@ -234,7 +261,9 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
                        int32_t compute_indices, void* out, float* lse, void* workspace,
                        size_t ws_bytes, hipStream_t stream) {
   if (!a || !shared_indices || (compute_indices != 0 && compute_indices != 1) ||
-      (a->index_fp8 != 0 && a->index_fp8 != 1))
+      (a->index_fp8 != 0 && a->index_fp8 != 1) || a->block_size < 0 ||
+      (a->block_size > 0 && (a->index_topk % a->block_size != 0 ||
+                             (a->pool != DSA_POOL_MAX && a->pool != DSA_POOL_MEAN))))
     return DSA_ERR_INVALID_ARG;
   const dsa_dtype idx_dt = a->index_fp8 ? DSA_FP8_E4M3 : a->dtype;
   dsa_status st = check_mla(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,
@@ -242,7 +271,7 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
   if (st != DSA_OK) return st;
   const Batch b = to_batch(batch);
   const size_t s_bytes = compute_indices ? scores_bytes(batch) : 0;
-  const size_t t_bytes = compute_indices ? align_up(dsa::topk_workspace_bytes(b, a->index_topk)) : 0;
+  const size_t t_bytes = compute_indices ? select_bytes(b, a->index_topk) : 0;
   const size_t m_bytes = mla_ws(batch, a->index_topk, a->n_heads, a->dtype);
   const size_t need = s_bytes + t_bytes + m_bytes;
   if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
@@ -262,8 +291,12 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
              : dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
                                   a->index_head_dim, a->dtype, scores, ld, stream);
     if (st != DSA_OK) return st;
-    st = dsa_topk(batch, scores, ld, a->index_topk, shared_indices, ws + s_bytes, t_bytes,
-                  stream);
+    st = a->block_size > 0
+             ? dsa_block_topk(batch, scores, ld, a->block_size, (dsa_pool)a->pool,
+                              a->index_topk / a->block_size, shared_indices, ws + s_bytes,
+                              t_bytes, stream)
+             : dsa_topk(batch, scores, ld, a->index_topk, shared_indices, ws + s_bytes, t_bytes,
+                        stream);
     if (st != DSA_OK) return st;
   }
   return dsa_sparse_mla_fwd(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,

@@ -267,6 +267,10 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
 // ---------------------------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+constexpr int F8_NSTEP = 4;                 // 32-key steps of one wave in a workgroup
+constexpr int F8_NBUF = 3;                  // steps of key rows in flight per wave
+constexpr int F8_KEYS_PER_BLOCK = F8_NSTEP * DEC_STEP * DEC_WAVES;
+
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -289,8 +293,7 @@ __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q
                                                    const float* __restrict__ w, int t,
                                                    int64_t kb0, int64_t s_beg, int64_t s_end,
                                                    float* __restrict__ srow, int stride,
-                                                   bool preloaded, Fp8Rows& b0, Fp8Rows& b1,
-                                                   Fp8Rows& b2) {
+                                                   bool preloaded, Fp8Rows (&buf)[F8_NBUF]) {
   constexpr int HI = 32 * HB;
   auto uni = [](int64_t x) {
     return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
@@ -338,17 +341,16 @@ __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q
   };
   if (s_beg >= s_end) return;
   if (!preloaded) {
-    load(s_beg, b0);
-    load(min(s_beg + stride, s_end - 1), b1);
-    load(min(s_beg + 2 * stride, s_end - 1), b2);
-  }
 #pragma unroll
-  for (int i = 0; i < DEC_NSTEP; ++i) {
+    for (int b = 0; b < F8_NBUF; ++b) load(min(s_beg + b * stride, s_end - 1), buf[b]);
+  }
+  // unrolled, so every buffer index is a compile-time constant (fixed registers)
+#pragma unroll
+  for (int i = 0; i < F8_NSTEP; ++i) {
     const int64_t s0 = s_beg + (int64_t)i * stride;
     if (s0 >= s_end) break;                      // uniform
-    Fp8Rows& cur = i % 3 == 0 ? b0 : (i % 3 == 1 ? b1 : b2);
-    step(s0, cur);
-    if (i + 3 < DEC_NSTEP) load(min(s0 + 3 * stride, s_end - 1), cur);
+    step(s0, buf[i % F8_NBUF]);
+    if (i + F8_NBUF < F8_NSTEP) load(min(s0 + F8_NBUF * stride, s_end - 1), buf[i % F8_NBUF]);
   }
 }
 
@@ -362,13 +364,13 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int j = blockIdx.y;
-  int64_t f = (int64_t)blockIdx.x * DEC_KEYS_PER_BLOCK;
-  const int64_t f_end = min(f + DEC_KEYS_PER_BLOCK, total_k);
-  // as in the bf16 kernel: the lookup's loads first, then the first three steps' key rows by
+  int64_t f = (int64_t)blockIdx.x * F8_KEYS_PER_BLOCK;
+  const int64_t f_end = min(f + F8_KEYS_PER_BLOCK, total_k);
+  // as in the bf16 kernel: the lookup's loads first, then the first steps' key rows by
   // flattened row
   const SeqBounds first = load_bounds(cu_q, cu_k, nseq, 0);
   __builtin_amdgcn_sched_barrier(0);
-  Fp8Rows b0, b1, b2;
+  Fp8Rows buf[F8_NBUF];
   {
     const uint8_t* kr = k_idx + 64 * (lane >> 5);
     auto pre = [&](int64_t r, Fp8Rows& dst) {
@@ -378,9 +380,8 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8(
       if constexpr (SCALED) dst.sc = k_scale[r];
     };
     const int64_t r0 = f + DEC_STEP * wave + (lane & 31);
-    pre(r0, b0);
-    pre(r0 + DEC_STEP * DEC_WAVES, b1);
-    pre(r0 + 2 * DEC_STEP * DEC_WAVES, b2);
+#pragma unroll
+    for (int b = 0; b < F8_NBUF; ++b) pre(r0 + b * DEC_STEP * DEC_WAVES, buf[b]);
   }
   auto segment = [&](auto preloaded) -> int64_t {
     const SeqSpan sp = seq_of_row<decltype(preloaded)::value>(cu_q, cu_k, nseq, f, first);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8(
       const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
       decode_segment_fp8<HB, SCALED>(q_idx, k_idx, k_scale, w, t, kb0, s_beg + DEC_STEP * wave,
                                      s_end, scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES,
-                                     decltype(preloaded)::value, b0, b1, b2);
+                                     decltype(preloaded)::value, buf);
     }
     return seg_end;
   };
@@ -690,7 +691,7 @@ hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_i
                               float* scores, int64_t ld, hipStream_t stream) {
   const uint8_t* q = (const uint8_t*)q_idx;
   const uint8_t* k = (const uint8_t*)k_idx;
-  dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK), b.max_q);
+  dim3 grid((unsigned)((b.total_k + F8_KEYS_PER_BLOCK - 1) / F8_KEYS_PER_BLOCK), b.max_q);
   auto go = [&](auto kern) {
     kern<<<grid, 256, 0, stream>>>(q, k, k_scale, w, b.cu_q, b.cu_k, b.nseq, b.total_q,
                                    b.total_k, scores, ld);

@@ -34,6 +34,14 @@ size_t topk_workspace_bytes(const Batch& b, int k);
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        void* workspace, hipStream_t stream);
 
+// Step 2, block-pooled: blocks of `block` positions scored by their max (or mean) score, the kb
+// best blocks' positions written to indices [T, kb * block]; workspace: block keys.
+bool block_topk_supported(const Batch& b, int block, int kb);
+size_t block_topk_workspace_bytes(const Batch& b, int block);
+hipError_t launch_block_topk(const Batch& b, const float* scores, int64_t ld, int block,
+                             bool mean, int kb, int32_t* indices, void* workspace,
+                             hipStream_t stream);
+
 // Step 3: sparse MLA (MQA) forward.
 struct MlaPlan {
   int nsplit;

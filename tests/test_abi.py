@@ -162,3 +162,20 @@ def test_fp8_indexer_rejects_bad_arguments(L):
                        None)                                   # index_fp8 must be 0 or 1
     assert L.dsa_forward(ctypes.byref(b), ctypes.byref(fa), FAKE, 1, FAKE, None, FAKE, 1 << 30,
                          None) == INVALID
+
+
+def test_block_topk_rejects_bad_arguments(L):
+    b = _batch()
+    f = L.dsa_block_topk
+    ok = [ctypes.byref(b), FAKE, 60, 64, 0, 32, FAKE, FAKE, 1 << 20, None]
+    for i, bad in ((1, None), (6, None), (2, 59), (5, 0), (4, 2)):
+        a = list(ok); a[i] = bad
+        assert f(*a) == INVALID, i
+    for bs in (3, 2, 512, 48):                     # block size: a power of two in 4..256
+        a = list(ok); a[3] = bs
+        assert f(*a) == UNSUPPORTED, bs
+    a = list(ok); a[5] = 1025
+    assert f(*a) == UNSUPPORTED
+    a = list(ok); a[7] = None
+    assert f(*a) == WORKSPACE
+    assert L.dsa_block_topk_workspace_size(ctypes.byref(b), 64) == 2 * 1 * 4   # 2 rows x 1 block
