@@ -429,7 +429,7 @@ def main():
 
     eb = 1 if fp8 else 2
     sb = step_bytes(case, eb)
-    ib, mb = indexer_bytes(case, eb), mla_bytes(case) // case.layers
+    ib, mb = indexer_bytes(case, eb), mla_bytes(case)          # one call = one layer
     kern = {"indexer": (launch_ms["indexer"], ib), "sparse_mla": (launch_ms["sparse_mla"], mb)}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
