@@ -217,6 +217,10 @@ typedef struct {
  * compute_indices = 0: shared_indices is read as cached by an earlier call of the group;
  *                      q_idx / k_idx / w are ignored and may be NULL.
  * With block_size > 0 the selection is dsa_block_topk's (index_topk a multiple of block_size).
+ * Per-position selection on the bf16 path with max_seqlen_k <= 16384 runs inside the sparse-MLA
+ * launch (each attention workgroup selects its own slice of shared_indices from the score row),
+ * so the top-k takes no launch of its own; shared_indices and the outputs are the same as with
+ * the separate calls, bit for bit.
  * The workspace holds the [T, max_seqlen_k] fp32 score matrix plus the selection and split-KV
  * scratch: dsa_workspace_size(DSA_OP_FORWARD, ...) bytes (enough for either selection). */
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* args,

@@ -291,6 +291,15 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
              : dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
                                   a->index_head_dim, a->dtype, scores, ld, stream);
     if (st != DSA_OK) return st;
+    const dsa::MlaPlan fplan = dsa::plan_sparse_mla_bf16(b, a->index_topk, a->n_heads);
+    if (a->block_size == 0 && a->dtype == DSA_BF16 && dsa::fused_select_supported(b, fplan)) {
+      // rows of at most 16384 positions: the sparse-MLA kernel selects each query's top-k in its
+      // prologue (one launch fewer); it writes shared_indices as dsa_topk would
+      return from_hip(dsa::launch_sparse_mla_bf16(b, a->q, a->kv, shared_indices, a->index_topk,
+                                                  a->n_heads, a->softmax_scale, out, lse,
+                                                  ws + s_bytes + t_bytes, fplan, stream, scores,
+                                                  ld));
+    }
     st = a->block_size > 0
              ? dsa_block_topk(batch, scores, ld, a->block_size, (dsa_pool)a->pool,
                               a->index_topk / a->block_size, shared_indices, ws + s_bytes,

@@ -98,24 +98,6 @@ __global__ __launch_bounds__(POOL_THREADS) void block_pool(
   }
 }
 
-// Exclusive prefix sum over the workgroup (every thread calls it); also returns the total.
-__device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t v, uint32_t* red, uint32_t& total) {
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan_u32(v);
-  if (lane_id() == WAVE - 1) red[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < BT_WAVES; ++w) {
-    const uint32_t x = red[w];
-    before += w < wave ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();                            // red may be reused right after
-  total = tot;
-  return before + incl - v;
-}
-
 // grid: x = query rows. Writes indices[t, 0 .. kb*B). The row's block keys are staged in LDS and
 // every pass over them runs as many steps as the row has blocks (four keys per thread and step,
 // loaded before use), so a short row costs a few hundred cycles per pass.
@@ -217,7 +199,7 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
       hs += h[j];
     }
     uint32_t total;
-    uint32_t above = wg_exclusive_sum(hs, red, total);
+    uint32_t above = wg_exclusive_sum<BT_WAVES>(hs, red, total);
     if (above < need && above + hs >= need) {   // exactly one thread
 #pragma unroll
       for (int j = 0; j < BT_BPT; ++j) {
@@ -270,9 +252,11 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
       ecount += __popc(eb[j]);
     }
     uint32_t tot;
-    const uint32_t e_before = wg_exclusive_sum(ecount, red, tot);
+    const uint32_t e_before = wg_exclusive_sum<BT_WAVES>(ecount, red, tot);
     // keep the lowest (need - e_before) equal blocks of these words
-    uint32_t keep = e_before >= need ? 0u : need - e_before, tcount = 0;
+    // (need - min(..) rather than a subtraction guarded by a comparison, which the compiler
+    // marks wrap-free and hoists)
+    uint32_t keep = need - min(e_before, need), tcount = 0;
 #pragma unroll
     for (int j = 0; j < BT_WPT; ++j) {
       while (keep > 0 && eb[j] != 0) {
@@ -283,7 +267,7 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
       }
       tcount += __popc(ab[j]);
     }
-    uint32_t r = wg_exclusive_sum(tcount, red, tot);
+    uint32_t r = wg_exclusive_sum<BT_WAVES>(tcount, red, tot);
 #pragma unroll
     for (int j = 0; j < BT_WPT; ++j) {
       uint32_t word = ab[j];

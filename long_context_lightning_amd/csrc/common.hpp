@@ -130,6 +130,26 @@ __device__ __forceinline__ uint32_t last_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
+// Exclusive prefix sum of v over a workgroup of NWAVES waves (every thread calls it); `red` is
+// NWAVES words of LDS; also returns the workgroup total. Two barriers.
+template <int NWAVES>
+__device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t v, uint32_t* red, uint32_t& total) {
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  if ((threadIdx.x & (WAVE - 1)) == WAVE - 1) red[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const uint32_t x = red[w];
+    before += w < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();                            // red may be reused right after
+  total = tot;
+  return before + incl - v;
+}
+
 // Largest b in [0, nseq) with cu[b] <= x (cu ascending, cu[0] <= x).
 template <typename I>
 __device__ __forceinline__ int find_seq(const I* __restrict__ cu, int nseq, int64_t x) {

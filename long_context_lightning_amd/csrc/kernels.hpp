@@ -49,10 +49,15 @@ struct MlaPlan {
   size_t workspace;
 };
 MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads);
+// With fused_scores, the top-k selection of each query runs in the kernel's prologue from the
+// score rows [T, ld_scores] and `indices` (then written, [T, k]) receives it; rows of at most
+// 16384 positions and splits of at most 2048 indices (fused_select_supported).
+bool fused_select_supported(const Batch& b, const MlaPlan& plan);
 hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
                                   const int32_t* indices, int k, int n_heads, float scale,
                                   void* out, float* lse, void* workspace, const MlaPlan& plan,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const float* fused_scores = nullptr,
+                                  int64_t ld_scores = 0);
 hipError_t launch_sparse_mla_f32(const Batch& b, const float* q, const float* kv,
                                  const int32_t* indices, int k, int n_heads, int d_qk, int d_v,
                                  float scale, float* out, float* lse, hipStream_t stream);

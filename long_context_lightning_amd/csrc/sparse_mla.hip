@@ -119,15 +119,220 @@ constexpr int ST_FLAG = 512;    // [8]           wave saw a logit beyond its ref
 // the wave is element 8*(q/4) + 4*kh + q%4; the other eight go to the partner wave.
 __device__ __forceinline__ int kept_elem(int q, int kh) { return 8 * (q >> 2) + 4 * kh + (q & 3); }
 
+// ---------------------------------------------------------------------------------------------
+// Fused selection (decode rows of at most FUSED_MAX_POS positions): every workgroup of a query
+// computes the query's top-k threshold from its score row and writes its own split's slice of
+// the index row, so the top-k needs no launch of its own. The selection rule is step 2's: the k
+// largest scores among positions 0..p (compared as reals, an equal score going to the lower
+// position), every position when p + 1 <= k, ascending. Thread i holds `per` consecutive
+// positions (8, 16 or 32, as the row bound needs) as order-preserving keys (0 marks a position
+// past the row).
+//   rounds: three radix digits of the key (bits 31..21, 20..10, 9..0), each counted in a
+//           2048-bin LDS histogram over the keys that share the digits found so far, give the
+//           threshold key (the k-th largest) and how many positions holding it are taken. Each
+//           round takes one barrier: its histogram was cleared in an earlier phase, and every
+//           wave finds the bin by itself (lane l sums 32 bins, a wave prefix sum picks the lane,
+//           then each lane takes one of that lane's bins and a second prefix sum picks the bin);
+//   ranks:  each thread's taken positions as a bit mask (scores at least the threshold; when
+//           ties at the threshold are not all taken, the extra equal ones are cleared from the
+//           highest positions down); a workgroup prefix sum of the mask populations gives each
+//           thread the rank of its first taken position, and only the bits whose ranks fall in
+//           the split's slice are written out.
+// ---------------------------------------------------------------------------------------------
+constexpr int FUSED_PER = 32;                                 // positions per thread, at most
+constexpr int FUSED_MAX_POS = FUSED_PER * NTHREADS;            // 16384
+constexpr int SEL_BINS = 2048;
+// bin b is stored at word b + b / 32 (one pad word after every 32 bins, so that lane l reading
+// the i-th bin of group l meets no other lane's bank), followed by one dummy bin per lane
+constexpr int SEL_PADDED = SEL_BINS + SEL_BINS / 32;
+constexpr int SEL_HIST = SEL_PADDED + WAVE;
+__device__ __forceinline__ uint32_t sel_slot(uint32_t b) { return b + (b >> 5); }
+constexpr int SEL_LIST = 2048;                 // longest slice of one split
+constexpr int SEL_H1 = SEL_HIST;                              // round 1's histogram
+constexpr int SEL_H2 = 2 * SEL_HIST;                          // round 2's
+constexpr int SEL_LIST_AT = 3 * SEL_HIST;
+constexpr int SEL_SCRATCH_WORDS = SEL_LIST_AT + SEL_LIST + 2 * NWAVES;
+static_assert(SEL_SCRATCH_WORDS * 4 <= STAGE_BYTES, "fused selection scratch must fit one stage");
+
+// Loads this thread's PER scores of the row, positions PER*tid .. PER*tid + PER - 1 (positions
+// past `lim` are left at 0 and masked later).
+template <int PER>
+__device__ __forceinline__ void fused_load_scores(const float* __restrict__ srow, int64_t lim,
+                                                  bool aligned, float (&v)[PER]) {
+  const int64_t p0 = (int64_t)threadIdx.x * PER;
+  if (aligned && p0 + PER <= lim) {
+#pragma unroll
+    for (int i = 0; i < PER / 4; ++i) {
+      const f32x4 x = *(const f32x4*)(srow + p0 + 4 * i);
+      v[4 * i] = x[0]; v[4 * i + 1] = x[1]; v[4 * i + 2] = x[2]; v[4 * i + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = p0 + i < lim ? srow[p0 + i] : 0.f;
+  }
+}
+
+// Searches bins 0..2047 (bin b at word sel_slot(b)) from the top for the one holding the need-th
+// largest key; every wave does it by itself and gets the same (bin, keys still needed inside
+// it). Subtractions are written so that none is guarded by a comparison: the compiler marks a
+// guarded one wrap-free, hoists it and then folds comparisons and minima with its operands away.
+__device__ __forceinline__ void fused_find_bin(const uint32_t* __restrict__ hc, uint32_t need,
+                                               uint32_t& bin, uint32_t& rem) {
+  const int lane = lane_id();
+  const int g = WAVE - 1 - lane;                         // this lane's bins 32g .. 32g + 31
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) sum += hc[33 * g + i];
+  const uint32_t above = wave_incl_scan_u32(sum) - sum;  // keys in the bins of lower lanes
+  const uint64_t hit = __ballot(above < need && above + sum >= need);
+  const int fl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  const uint32_t above_fl = __builtin_amdgcn_readlane(above, fl);
+  // lane j (< 32) takes bin top - j of lane fl's 32 bins
+  const int gf = WAVE - 1 - fl;
+  const uint32_t h = lane < 32 ? hc[33 * gf + 31 - lane] : 0u;
+  const uint32_t cum = above_fl + wave_incl_scan_u32(h) - h;
+  const uint64_t hit2 = __ballot(cum < need && cum + h >= need);
+  const int j = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit2));
+  bin = (uint32_t)(32 * gf + 31 - j);
+  rem = need - min(__builtin_amdgcn_readlane(cum, j), need);
+}
+
+// Clears the histograms of rounds 0 and 1 in the fused selection's scratch (before a barrier
+// that precedes fused_select_slice).
+__device__ __forceinline__ void fused_clear(uint32_t* __restrict__ scratch) {
+  for (int i = threadIdx.x; i < SEL_H2; i += NTHREADS) scratch[i] = 0;
+}
+
+// Writes idx_row[r] for r in [r_beg, r_end) (r_end - r_beg <= SEL_LIST) from the scores v of
+// positions 0..n-1 (fused_load_scores). scratch: SEL_SCRATCH_WORDS words of LDS whose first two
+// histograms fused_clear zeroed before a barrier. Every thread of the workgroup calls it.
+template <int PER>
+__device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_t n, int k,
+                                                   int r_beg, int r_end, int32_t* idx_row,
+                                                   uint32_t* __restrict__ scratch) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = lane_id();
+  uint32_t* list = scratch + SEL_LIST_AT;      // [SEL_LIST] the split's slice
+  uint32_t* red = list + SEL_LIST;             // [2][NWAVES] prefix-sum partials
+  if (n <= k) {                                // dense: every visible position
+    for (int r = r_beg + tid; r < r_end; r += NTHREADS) idx_row[r] = r < n ? r : -1;
+    return;
+  }
+  const int64_t p0 = (int64_t)tid * PER;
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = p0 + i < n ? score_key(v[i]) : 0u;  // never 0
+  // round 0: bits 31..21 of every key (a position past the row counts in its lane's dummy bin)
+  uint32_t need = (uint32_t)k, bin;
+  {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      atomicAdd(&scratch[key[i] ? sel_slot(key[i] >> 21) : SEL_PADDED + lane], 1u);
+    __syncthreads();
+    fused_find_bin(scratch, need, bin, need);
+  }
+  uint32_t pref = bin;                         // bits 31..21 of the threshold
+  // round 1: bits 20..10 of the keys sharing them (H1; H2 is cleared meanwhile)
+  {
+    uint32_t* hc = scratch + SEL_H1;
+    for (int i = tid; i < SEL_HIST; i += NTHREADS) scratch[SEL_H2 + i] = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((key[i] >> 21) == pref) atomicAdd(&hc[sel_slot((key[i] >> 10) & 2047u)], 1u);
+    __syncthreads();
+    fused_find_bin(hc, need, bin, need);
+  }
+  pref = (pref << 11) | bin;                   // bits 31..10
+  // round 2: bits 9..0 (H2; bins 1024.. stay empty)
+  {
+    uint32_t* hc = scratch + SEL_H2;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((key[i] >> 10) == pref) atomicAdd(&hc[sel_slot(key[i] & 1023u)], 1u);
+    __syncthreads();
+    fused_find_bin(hc, need, bin, need);
+  }
+  const uint32_t lo = (pref << 10) | bin;
+  const uint32_t thr = lo;                     // the k-th largest key; `need` positions holding it
+  uint32_t ge = 0;                             // are taken
+#pragma unroll
+  for (int i = 0; i < PER; ++i) ge |= (key[i] >= thr ? 1u : 0u) << i;
+  uint32_t cnt = __popc(ge);
+  uint32_t incl = wave_incl_scan_u32(cnt);
+  if (lane == WAVE - 1) red[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const uint32_t x = red[w];
+    before += w < wave ? x : 0u;
+    total += x;
+  }
+  if (total > (uint32_t)k) {                   // uniform: ties at the threshold not all taken
+    // the taken equal keys are the first `need` in position order: drop this thread's last
+    // (its equal keys past the need-th) from the mask
+    uint32_t eq = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) eq |= (key[i] == thr ? 1u : 0u) << i;
+    const uint32_t n_eq = __popc(eq);
+    const uint32_t e_incl = wave_incl_scan_u32(n_eq);
+    if (lane == WAVE - 1) red[NWAVES + wave] = e_incl;
+    __syncthreads();
+    uint32_t e_before = e_incl - n_eq;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) e_before += w < wave ? red[NWAVES + w] : 0u;
+    const uint32_t e_taken_before = min(e_before, need);
+    uint32_t drop = n_eq - min(n_eq, need - e_taken_before);
+    while (drop > 0) {                         // clear the highest equal positions
+      const uint32_t top = 1u << (31 - __builtin_clz(eq));
+      eq ^= top;
+      ge ^= top;
+      --drop;
+    }
+    // ranks: keys above the threshold before this thread, plus the equal ones taken before it
+    uint32_t gt_cnt = __popc(ge) - min(n_eq, need - e_taken_before);
+    const uint32_t g_incl = wave_incl_scan_u32(gt_cnt);
+    if (lane == WAVE - 1) red[wave] = g_incl;  // (every wave read red[0..7] before the barrier
+    __syncthreads();                           //  above)
+    before = g_incl - gt_cnt + e_taken_before;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) before += w < wave ? red[w] : 0u;
+  }
+  // write the taken positions whose ranks fall in [r_beg, r_end)
+  uint32_t rk = before;
+  uint32_t m = ge;
+  // skip the taken positions ranked before r_beg
+  uint32_t skip = min((uint32_t)r_beg - min(rk, (uint32_t)r_beg), (uint32_t)__popc(m));
+  rk += skip;
+  while (skip > 0) {
+    m &= m - 1;
+    --skip;
+  }
+  while (m != 0 && rk < (uint32_t)r_end) {
+    const int i = __builtin_ctz(m);
+    list[rk - r_beg] = (uint32_t)(tid * PER + i);
+    m &= m - 1;
+    ++rk;
+  }
+  __syncthreads();
+  for (int j = tid; j < r_end - r_beg; j += NTHREADS) idx_row[r_beg + j] = (int32_t)list[j];
+}
+
 // grid: 1-D, 8 * ceil(T/8) * nsplit * ceil(H/64) workgroups. Consecutive workgroups are
 // dispatched round-robin to the 8 XCDs; the mapping gives every workgroup of one query the same
 // XCD, so the query block and the split partials of a query stay in one L2.
+// FPER > 0: the split's indices are selected from `scores` in the prologue (fused_select_slice,
+// FPER positions per thread)
+// and written to `indices` (the caller's index row) before the tiles read them back.
+template <int FPER>
 __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ indices, int k, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int H,
     float scale_log2, int nsplit, int rows_per_split, __bf16* __restrict__ out,
-    float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse,
+    const float* __restrict__ scores, int64_t ld_scores, int32_t* idx_out) {
+  constexpr bool FUSED = FPER > 0;
   // Separate LDS objects let the compiler see that the gathers streaming into one stage never
   // alias reads of the other stage or of the exchange region, so it adds no waits of its own.
   __shared__ __attribute__((aligned(16))) char stage0[STAGE_BYTES];
@@ -158,15 +363,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
 
   const int r_beg = split * rows_per_split;
   const int r_end = min(k, r_beg + rows_per_split);
-  const int32_t* irow = indices + (int64_t)t * k;
+  // with FUSED the index row is written by this kernel (idx_out, not restrict-qualified) and
+  // read back from it
+  const int32_t* irow = (FUSED ? (const int32_t*)idx_out : indices) + (int64_t)t * k;
   // The first two tiles' indices do not depend on the sequence lookup, so their loads go out
   // before it and the latencies overlap. (Loaded even if the split turns out to be empty: every
   // address is inside its array.) The query block is loaded behind the first gathers.
   bf16x8 qreg[QK_STEPS];
-  int i_even = irow[min(r_beg + lane, k - 1)];          // indices of the next even / odd tile
-  int i_odd = irow[min(r_beg + TILE + lane, k - 1)];
+  int i_even = 0, i_odd = 0;                            // indices of the next even / odd tile
+  if constexpr (!FUSED) {
+    i_even = irow[min(r_beg + lane, k - 1)];
+    i_odd = irow[min(r_beg + TILE + lane, k - 1)];
+  }
   // The sequence lookup is done by one wave and shared through LDS: every workgroup of the grid
   // starts at once and reads the same few cache lines of cu_seqlens.
+  float fs[FUSED ? FPER : 1];                           // this thread's scores (FUSED)
+  if constexpr (FUSED)                                  // issued before the sequence lookup
+    fused_load_scores<FPER>(scores + (int64_t)t * ld_scores,
+                            min(ld_scores, (int64_t)FUSED_MAX_POS), (ld_scores & 3) == 0, fs);
+  if constexpr (FUSED) fused_clear((uint32_t*)stage0);   // (ordered by the lookup's barrier)
   QueryPos qp;
   {
     int64_t* qs = (int64_t*)rbuf;
@@ -183,6 +398,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     qp.key_base = qs[1];
     qp.len = qs[2];
     qp.b = 0;
+  }
+  if constexpr (FUSED) {
+    // this split's slice of the index row, then the first two tiles' indices read back (the
+    // barrier's workgroup fence orders the stores before the loads)
+    const int64_t n = qp.p >= 0 ? min(min(qp.p + 1, ld_scores), (int64_t)FUSED_MAX_POS) : 0;
+    fused_select_slice<FPER>(fs, n, k, r_beg, r_end, idx_out + (int64_t)t * k, (uint32_t*)stage0);
+    __syncthreads();
+    i_even = irow[min(r_beg + lane, k - 1)];
+    i_odd = irow[min(r_beg + TILE + lane, k - 1)];
   }
   const int64_t L = qp.len;
   const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);
@@ -718,6 +942,10 @@ __global__ __launch_bounds__(256) void sparse_mla_f32(
 
 }  // namespace
 
+bool fused_select_supported(const Batch& b, const MlaPlan& plan) {
+  return b.max_k <= FUSED_MAX_POS && plan.rows_per_split <= SEL_LIST;
+}
+
 MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
   MlaPlan p;
   const int tiles = (k + TILE - 1) / TILE;
@@ -739,7 +967,8 @@ MlaPlan plan_sparse_mla_bf16(const Batch& b, int k, int n_heads) {
 hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
                                   const int32_t* indices, int k, int n_heads, float scale,
                                   void* out, float* lse, void* workspace, const MlaPlan& plan,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const float* fused_scores,
+                                  int64_t ld_scores) {
   float* part_lse = nullptr;
   __bf16* part_o = nullptr;
   if (plan.nsplit > 1) {
@@ -749,10 +978,22 @@ hipError_t launch_sparse_mla_bf16(const Batch& b, const void* q, const void* kv,
   const int tgroups = (b.total_q + 7) / 8;
   const int64_t nblocks =
       (int64_t)8 * tgroups * plan.nsplit * ((n_heads + WG_HEADS - 1) / WG_HEADS);
-  sparse_mla_bf16<<<dim3((unsigned)nblocks), NTHREADS, 0, stream>>>(
-      (const __bf16*)q, (const __bf16*)kv, indices, k, b.cu_q, b.cu_k, b.nseq, b.total_q,
-      b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, (__bf16*)out, lse,
-      part_o, part_lse);
+  auto run = [&](auto kern, const float* sc, int64_t ld, int32_t* idx_out) {
+    kern<<<dim3((unsigned)nblocks), NTHREADS, 0, stream>>>(
+        (const __bf16*)q, (const __bf16*)kv, indices, k, b.cu_q, b.cu_k, b.nseq, b.total_q,
+        b.total_k, n_heads, scale * kLog2e, plan.nsplit, plan.rows_per_split, (__bf16*)out, lse,
+        part_o, part_lse, sc, ld, idx_out);
+  };
+  if (fused_scores) {
+    // positions per thread: the fewest that cover the row bound
+    const int64_t lim = std::min<int64_t>(ld_scores, FUSED_MAX_POS);
+    int32_t* idx_out = const_cast<int32_t*>(indices);
+    if (lim <= 8 * NTHREADS) run(sparse_mla_bf16<8>, fused_scores, ld_scores, idx_out);
+    else if (lim <= 16 * NTHREADS) run(sparse_mla_bf16<16>, fused_scores, ld_scores, idx_out);
+    else run(sparse_mla_bf16<32>, fused_scores, ld_scores, idx_out);
+  } else {
+    run(sparse_mla_bf16<0>, nullptr, 0, nullptr);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
   // P threads per 8-column piece, each merging at most CMB_SPLITS splits

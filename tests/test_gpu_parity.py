@@ -659,3 +659,47 @@ def test_reference_max_restart_path():
         say(f"  restart path, query {i}: max|d|={a:.3e} (max|ref| {np.abs(r).max():.1f}) "
             f"rel={rel:.3e}")
         assert ok, (i, a, rel)
+
+
+@pytest.mark.parametrize("lens,nq,kw", [
+    ((16384,) * 32, (1,) * 32, {}),                                   # the decode workload shape
+    ((1, 2047, 2048, 2049, 16384, 9000), (1, 1, 1, 1, 1, 1), {}),      # around the dense threshold
+    ((5000, 16384, 3000, 12000), (2, 4, 1, 3), {}),                   # several queries per row
+    ((16384, 9000, 7000), (1, 1, 1), {"idx_range": 1, "w_range": 1}),  # heavy ties
+    ((9000, 16000), (1, 1), {"index_topk": 4096}),                    # 32 splits of two tiles
+    ((5000, 7000, 16384), (1, 1, 1), {"index_topk": 3000}),           # k not a multiple of 64
+    ((16384, 6000), (1, 2), {"n_heads": 128}),                         # two head groups per split
+    ((16384, 6000, 3333), (1, 1, 1), {"n_heads": 32}),
+])
+def test_forward_fused_selection_matches_topk(lens, nq, kw):
+    """dsa_forward on rows of at most 16384 positions selects the top-k inside the sparse-MLA
+    kernel: the shared indices must equal dsa_topk's on the same scores and the oracle's, and the
+    outputs those of the separate sparse-MLA call, bit for bit."""
+    case = _small_case(f"fused_{lens}_{nq}_{sorted(kw.items())}", lens, nq, **kw)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    o, l, shared = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                               case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    idx = dsa.topk(scores, batch, case.index_topk)
+    o2, l2 = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], idx, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(shared, idx)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    rows = range(case.total_q) if case.total_q <= 12 else [0, 7, 19, case.total_q - 1]
+    check_rows(case, d, scores, shared, {0: o}, {0: l}, rows)
+
+
+def test_forward_fused_selection_equal_scores():
+    """Every score equal (zero weights; signed zeros among them): the fused selection takes the
+    lowest positions, like dsa_topk."""
+    case = _small_case("fused_ties", (9000, 16384, 3000), (1, 2, 1))
+    d = DI.make_inputs(case, "cuda")
+    d["w"].zero_()
+    d["q_idx"][:, :, ::2] *= -1
+    batch = batch_of(case, d)
+    _, _, shared = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                               case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    torch.cuda.synchronize()
+    want = torch.arange(case.index_topk, device="cuda", dtype=torch.int32)
+    assert bool((shared == want[None, :]).all())
