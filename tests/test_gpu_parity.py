@@ -661,6 +661,38 @@ def test_reference_max_restart_path():
         assert ok, (i, a, rel)
 
 
+def test_split_partials_against_one_split():
+    """The error the bf16 split partials add: one decode query attended once alone (16 splits of
+    two tiles, partials in bf16 merged by mla_combine) and once as one of 256 identical queries
+    of a batch (one split: no partials), both against the oracle and against each other."""
+    L, k, H = 16384, 2048, 64
+    kv = DI.normal((L, 576), 0.1, torch.bfloat16, "cuda", 9101)
+    q1 = DI.normal((1, H, 576), 0.1, torch.bfloat16, "cuda", 9102)
+    g = torch.Generator(device="cpu").manual_seed(9103)
+    sel = torch.sort(torch.randperm(L - 256, generator=g)[:k]).values.to(torch.int32)
+    scale = 1 / 24
+    outs = {}
+    for T in (1, 256):
+        batch = dsa.Batch.from_lengths([T], [L], device="cuda")
+        q = q1.expand(T, H, 576).contiguous()
+        idx = sel.to("cuda")[None, :].expand(T, k).contiguous()
+        out, lse = dsa.sparse_mla_fwd(q, kv, idx, batch, scale, 512)
+        torch.cuda.synchronize()
+        outs[T] = (out[0].float().cpu().numpy(), lse[0].float().cpu().numpy())
+        if T == 256:   # every copy of the query got the same bits
+            assert bool((out == out[0:1]).all())
+    ref, ref_lse = O.sparse_attention_row(host64(q1[0]), host64(kv[sel.long().to("cuda")]), 512,
+                                          scale)
+    a16, r16 = attn_errors(outs[1][0], ref)
+    a1, r1 = attn_errors(outs[256][0], ref)
+    ad, rd = attn_errors(outs[1][0], outs[256][0])
+    say(f"  16 splits vs oracle: max|d|={a16:.3e} rel={r16:.3e}; one split vs oracle: "
+        f"max|d|={a1:.3e} rel={r1:.3e}; 16 vs 1 split: max|d|={ad:.3e} rel={rd:.3e}; "
+        f"lse 16 vs 1 split max|d|={np.abs(outs[1][1] - outs[256][1]).max():.3e}")
+    assert attn_close(outs[1][0], ref)[0] and attn_close(outs[256][0], ref)[0]
+    assert np.allclose(outs[1][1], ref_lse, rtol=1e-4, atol=2e-3)
+
+
 @pytest.mark.parametrize("lens,nq,kw", [
     ((16384,) * 32, (1,) * 32, {}),                                   # the decode workload shape
     ((1, 2047, 2048, 2049, 16384, 9000), (1, 1, 1, 1, 1, 1), {}),      # around the dense threshold
