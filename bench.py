@@ -433,6 +433,9 @@ def main():
     kern = {"indexer": (launch_ms["indexer"], ib), "sparse_mla": (launch_ms["sparse_mla"], mb)}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
+    # the profile whose traffic record applies: workload, indexer dtype, selection kind
+    prof = (args.workload + ("_fp8" if fp8 else "")
+            + (f"_block{args.block_size}_{args.pool}" if blk else ""))
     if max(case.seqlens_q) > 1 and case.dtype == torch.bfloat16:
         # prefill: many queries share each key row, so the calls are matrix-core bound
         dflops = indexer_flops(case) if dom == "indexer" else mla_flops(case)
@@ -440,13 +443,13 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_record(args.workload + ("_fp8" if fp8 else ""), dom), "traffic_unit": "B/launch",
+                "traffic": traffic_record(prof, dom), "traffic_unit": "B/launch",
                 "algorithmic_flops_per_launch": dflops, "avg_launch_ms": round(dms, 5)}
     else:
         achieved = dbytes / (dms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_record(args.workload + ("_fp8" if fp8 else ""), dom), "traffic_unit": "B/launch",
+                "traffic": traffic_record(prof, dom), "traffic_unit": "B/launch",
                 "algorithmic_bytes_per_launch": dbytes,
                 "avg_launch_ms": round(dms, 5)}
     line = {
