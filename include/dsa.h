@@ -22,11 +22,12 @@
  *   - All tensors are dense row-major device buffers owned by the caller. The library never
  *     allocates, frees or synchronises on a call path; each call only enqueues work on `stream`
  *     and returns. Scratch memory comes from a caller-provided workspace whose size is given by
- *     dsa_workspace_size(). The only mutable global state is one write-only device
- *     array of the prefill indexer: lanes with no score to store (causally masked keys, keys or
- *     queries past a sequence) store into it, so every key tile issues the same number of
- *     stores; it is never read, so concurrent calls on several streams store into it without
- *     affecting any result.
+ *     dsa_workspace_size(). Mutable global state: (1) one write-only device array of the
+ *     prefill indexer: lanes with no score to store (causally masked keys, keys or queries past
+ *     a sequence) store into it, so every key tile issues the same number of stores; it is
+ *     never read, so concurrent calls on several streams store into it without affecting any
+ *     result; (2) the scratch array of dsa_sparse_mla_fwd_noalloc (see there), used by that
+ *     call only.
  *   - All argument checks run on the host before anything is enqueued; a non-zero status means
  *     nothing was launched. Device-resident values (cu_seqlens) cannot be checked without a
  *     synchronisation: the caller guarantees they are consistent with the host-side sizes, and
