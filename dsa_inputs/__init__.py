@@ -5,7 +5,8 @@ This module draws random tensors and lays out ragged batches. It holds none of t
 method's arithmetic: no scoring, selection or attention happens here.
 
 Every tensor comes from its own torch generator seeded with ``1000*case + tensor_id``
-(ids: k_idx=1, q_idx=2, w=3, kv of layer l = 10+l, q of layer l = 20+l). Integer-valued
+(ids: k_idx=1, q_idx=2, w=3, kv of layer l = 10+l, q of layer l = 20+l, the share mask of
+correlated query tokens = 4). Integer-valued
 tensors are drawn uniformly over the inclusive integer range and cast to the case dtype
 (exact). Normal tensors are ``randn * sigma`` rounded once to the case dtype. Tensors are
 generated on the requested device; the oracle always receives a host copy of exactly the
@@ -20,7 +21,7 @@ from typing import Dict, List, Optional
 import numpy as np
 import torch
 
-ID_K_IDX, ID_Q_IDX, ID_W = 1, 2, 3
+ID_K_IDX, ID_Q_IDX, ID_W, ID_SHARE = 1, 2, 3, 4
 ID_KV0, ID_Q0 = 10, 20
 
 
@@ -42,6 +43,8 @@ class Case:
     d_v: int                  # value width (leading columns of the latent row)
     sigma: float              # q, kv ~ N(0, sigma^2)
     layers: int = 1           # sparse-MLA layers sharing one index pass
+    q_share: float = 0.0      # later query tokens of a sequence copy this fraction of their
+    #                           indexer entries (q_I, w) from the token before them
 
     @property
     def batch(self) -> int:
@@ -86,6 +89,13 @@ CASES: Dict[str, Case] = {
     # long-context decode, one index pass shared by 4 sparse-MLA layers
     "indexshare_b8_l256k": Case("indexshare_b8_l256k", 4000, torch.bfloat16, (262144,) * 8,
                                 (1,) * 8, layers=4, **_GLM_DIMS),
+    # multi-token (MTP) decode: 32 sequences of 16384 tokens, 4 new query tokens each, drawn
+    # independently, and the same with 90% of each token's indexer entries shared with the one
+    # before it
+    "mtp_b32_l16k_q4": Case("mtp_b32_l16k_q4", 6000, torch.bfloat16, (16384,) * 32, (4,) * 32,
+                            **_GLM_DIMS),
+    "mtp_b32_l16k_q4_shared": Case("mtp_b32_l16k_q4_shared", 6000, torch.bfloat16,
+                                   (16384,) * 32, (4,) * 32, q_share=0.9, **_GLM_DIMS),
     # mixed-length decode, 16 sequences log-uniform in [512, 1048576]
     "mixed_b16_l512_1m": Case("mixed_b16_l512_1m", 5000, torch.bfloat16,
                               tuple(mixed_lengths()), (1,) * 16, **_GLM_DIMS),
@@ -158,6 +168,19 @@ def make_inputs(case: Case, device="cpu", layers: Optional[int] = None) -> Dict[
         cu_seqlens_q=cu_seqlens(case.seqlens_q, torch.int32).to(device),
         cu_seqlens_k=cu_seqlens(case.seqlens_k, torch.int64).to(device),
     )
+    if case.q_share > 0:
+        # correlated query tokens of one sequence (speculative decoding drafts several tokens
+        # whose selections overlap): token j > 0 takes each entry of q_I and w from token j-1
+        # with probability q_share, element by element, from a generator of its own
+        g = _gen(device, sb + ID_SHARE)
+        mq = torch.rand(d["q_idx"].shape, generator=g, device=device) < case.q_share
+        mw = torch.rand(d["w"].shape, generator=g, device=device) < case.q_share
+        t = 0
+        for nq in case.seqlens_q:
+            for j in range(1, nq):
+                d["q_idx"][t + j] = torch.where(mq[t + j], d["q_idx"][t + j - 1], d["q_idx"][t + j])
+                d["w"][t + j] = torch.where(mw[t + j], d["w"][t + j - 1], d["w"][t + j])
+            t += nq
     return d
 
 

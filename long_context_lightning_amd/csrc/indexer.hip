@@ -54,12 +54,18 @@ constexpr int DEC_NSTEP = DEC_KEYS_PER_WAVE / DEC_STEP;   // steps of one wave i
 // With `preloaded`, b0..b2 already hold the first three steps' rows (loaded by flattened row
 // before the sequence lookup: rows past the sequence belong to the next one, and their scores
 // are computed but never stored).
-template <int HB>
+// NQ > 1 (several new tokens of one sequence, e.g. multi-token prediction): queries t .. t+NQ-1
+// share the key stream, each key step multiplied by every query's operands, so a key row is
+// read once for all of them; query t+j (j < nvalid) at position p_first + j stores the keys
+// below min(s_lim, p_first + j + 1), and s_end (the stream's end) is that bound of the last
+// valid query. Queries j >= nvalid compute on query t's operands and store nothing.
+template <int HB, int NQ = 1>
 __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
                                                const __bf16* __restrict__ k_idx,
-                                               const float* __restrict__ w, int t, int64_t kb0,
+                                               const float* __restrict__ w, int t, int nvalid,
+                                               int64_t p_first, int64_t s_lim, int64_t kb0,
                                                int64_t s_beg, int64_t s_end,
-                                               float* __restrict__ srow, int stride,
+                                               float* __restrict__ scores, int64_t ld, int stride,
                                                bool preloaded, bf16x8 (&b0)[8], bf16x8 (&b1)[8],
                                                bf16x8 (&b2)[8], bf16x8* __restrict__ xw) {
   constexpr int HI = 32 * HB;
@@ -78,15 +84,22 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  bf16x8 a[HB][8];
-  float wr[HB][16];
+  bf16x8 a[NQ][HB][8];
+  float wr[NQ][HB][16];
+  int64_t s_q[NQ];                               // store bound of each query
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const __bf16* qr = q_idx + ((int64_t)t * HI + hb * 32 + col) * D + half * 8;
+  for (int j = 0; j < NQ; ++j) {
+    const int tj = t + (j < nvalid ? j : 0);
+    s_q[j] = j < nvalid ? uni(min(s_lim, p_first + j + 1)) : 0;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) a[hb][st] = *(const bf16x8*)(qr + st * 16);
+    for (int hb = 0; hb < HB; ++hb) {
+      const __bf16* qr = q_idx + ((int64_t)tj * HI + hb * 32 + col) * D + half * 8;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wr[hb][r] = w[(int64_t)t * HI + hb * 32 + mfma32_row(r, lane)];
+      for (int st = 0; st < 8; ++st) a[j][hb][st] = *(const bf16x8*)(qr + st * 16);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        wr[j][hb][r] = w[(int64_t)tj * HI + hb * 32 + mfma32_row(r, lane)];
+    }
   }
 
   // Key rows are read coalesced: load st of a step covers rows 4*st .. 4*st+3 of its 32, lane l
@@ -110,18 +123,21 @@ __device__ __forceinline__ void decode_segment(const __bf16* __restrict__ q_idx,
     }
 #pragma unroll
     for (int st = 0; st < 8; ++st) bop[st] = xw[col * 16 + ((2 * st + half) ^ (col & 15))];
-    float v = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[hb][st], bop[st], acc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], relu(acc[r]), v);
-    }
-    v += __shfl_xor(v, 32, WAVE);
     const int64_t s = s0 + col;
-    if (half == 0 && s < s_end) srow[s] = v;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) acc = mfma32x32x16(a[j][hb][st], bop[st], acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaf(wr[j][hb][r], relu(acc[r]), v);
+      }
+      v += __shfl_xor(v, 32, WAVE);
+      if (half == 0 && s < s_q[j]) scores[(int64_t)(t + j) * ld + s] = v;
+    }
   };
   // three buffers with fixed register names (a rotating copy would wait for the loads), so
   // two steps of key rows stay in flight while one is multiplied
@@ -197,8 +213,9 @@ __device__ __forceinline__ SeqSpan seq_of_row(const int32_t* __restrict__ cu_q,
   return r;
 }
 
-// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = query offset j within its sequence.
-template <int HB>
+// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = group of NQ query offsets within its
+// sequence (NQ consecutive new tokens share the key stream).
+template <int HB, int NQ>
 __global__ __launch_bounds__(256) void indexer_decode_bf16(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
     const float* __restrict__ w, const int32_t* __restrict__ cu_q,
@@ -242,14 +259,17 @@ __global__ __launch_bounds__(256) void indexer_decode_bf16(
     if (kb1 <= f || kb0 > f) return f_end;
     const int64_t seg_end = min(f_end, kb1);
     const int nq = q1 - q0;
-    if (j < nq && q0 + j < total_q && q0 + j >= 0) {
-      const int t = q0 + j;
-      const int64_t p = (kb1 - kb0) - nq + j;
+    const int j0 = j * NQ;                       // first query offset of this group
+    if (j0 < nq && q0 + j0 >= 0 && q0 + nq <= total_q) {
+      const int t = q0 + j0;
+      const int nvalid = min(NQ, nq - j0);
+      const int64_t p_first = (kb1 - kb0) - nq + j0;
       const int64_t s_beg = f - kb0;
-      const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
-      decode_segment<HB>(q_idx, k_idx, w, t, kb0, s_beg + DEC_STEP * wave, s_end,
-                         scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES, decltype(preloaded)::value,
-                         b0, b1, b2, xbuf[wave]);
+      const int64_t s_lim = min(seg_end - kb0, ld);
+      const int64_t s_end = min(s_lim, p_first + nvalid);
+      decode_segment<HB, NQ>(q_idx, k_idx, w, t, nvalid, p_first, s_lim, kb0,
+                             s_beg + DEC_STEP * wave, s_end, scores, ld, DEC_STEP * DEC_WAVES,
+                             decltype(preloaded)::value, b0, b1, b2, xbuf[wave]);
     }
     return seg_end;
   };
@@ -675,13 +695,20 @@ hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_
       indexer_prefill_bf16<2><<<grid, PF_THREADS, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
                                                                b.total_q, b.total_k, scores, ld);
   } else {
-    dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK), b.max_q);
-    if (index_n_heads == 32)
-      indexer_decode_bf16<1><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
-                                                       b.total_q, b.total_k, scores, ld);
-    else
-      indexer_decode_bf16<2><<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq,
-                                                       b.total_q, b.total_k, scores, ld);
+    // 32 indexer heads: up to four new tokens of a sequence share one key stream (their
+    // operands stay in registers); 64 heads: one token per stream
+    const int nq = index_n_heads == 32 ? std::min(b.max_q, 4) : 1;
+    dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK),
+              (unsigned)((b.max_q + nq - 1) / nq));
+    auto go = [&](auto kern) {
+      kern<<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k,
+                                     scores, ld);
+    };
+    if (index_n_heads == 64) go(indexer_decode_bf16<2, 1>);
+    else if (nq == 1) go(indexer_decode_bf16<1, 1>);
+    else if (nq == 2) go(indexer_decode_bf16<1, 2>);
+    else if (nq == 3) go(indexer_decode_bf16<1, 3>);
+    else go(indexer_decode_bf16<1, 4>);
   }
   return hipGetLastError();
 }

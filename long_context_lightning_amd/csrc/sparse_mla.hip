@@ -320,7 +320,10 @@ __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_
 
 // grid: 1-D, 8 * ceil(T/8) * nsplit * ceil(H/64) workgroups. Consecutive workgroups are
 // dispatched round-robin to the 8 XCDs; the mapping gives every workgroup of one query the same
-// XCD, so the query block and the split partials of a query stay in one L2.
+// XCD, so the query block and the split partials of a query stay in one L2, and gives each XCD
+// a run of consecutive queries (XCD x: queries x*ceil(T/8) ..), worked through in order, so the
+// queries of one sequence (several decode tokens, a prefill chunk) meet in one L2 and the rows
+// they select in common are fetched from HBM once.
 // FPER > 0: the split's indices are selected from `scores` in the prologue (fused_select_slice,
 // FPER positions per thread)
 // and written to `indices` (the caller's index row) before the tiles read them back.
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   const int kk = blockIdx.x >> 3;
   const int hg = kk % nhg;
   const int split = (kk / nhg) % nsplit;
-  const int t = (kk / nhg / nsplit) * 8 + xcd;
+  const int t = xcd * ((total_q + 7) >> 3) + kk / nhg / nsplit;
   if (t >= total_q) return;
 
   const int tid = threadIdx.x;

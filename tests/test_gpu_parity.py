@@ -173,6 +173,25 @@ def test_decode_b32_l16k_all_rows():
     check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
 
 
+@pytest.mark.parametrize("name", ["mtp_b32_l16k_q4", "mtp_b32_l16k_q4_shared"])
+def test_mtp_decode_all_rows(name):
+    """Four new tokens per sequence (one key stream scored for all four, in the indexer): every
+    row against the oracle, through the separate calls and through dsa_forward (top-k inside
+    the sparse-MLA launch)."""
+    case = DI.CASES[name]
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores, idx, out, lse = run_path(case, d, batch)
+    row_properties(case, idx)
+    check_rows(case, d, scores, idx, {0: out}, {0: lse}, range(case.total_q))
+    o2, l2, i2 = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                             case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    torch.cuda.synchronize()
+    assert torch.equal(i2, idx)
+    assert torch.equal(o2, out) and torch.equal(l2, lse)
+
+
 def test_decode_forward_matches_separate_calls():
     case = DI.CASES["decode_b32_l16k"]
     d = DI.make_inputs(case, "cuda")
