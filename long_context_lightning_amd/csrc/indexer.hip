@@ -306,14 +306,17 @@ __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int HB, bool SCALED>
+// NQ: as decode_segment (queries t .. t+NQ-1 share the key stream).
+template <int HB, bool SCALED, int NQ = 1>
 __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q_idx,
                                                    const uint8_t* __restrict__ k_idx,
                                                    const float* __restrict__ k_scale,
                                                    const float* __restrict__ w, int t,
+                                                   int nvalid, int64_t p_first, int64_t s_lim,
                                                    int64_t kb0, int64_t s_beg, int64_t s_end,
-                                                   float* __restrict__ srow, int stride,
-                                                   bool preloaded, Fp8Rows (&buf)[F8_NBUF]) {
+                                                   float* __restrict__ scores, int64_t ld,
+                                                   int stride, bool preloaded,
+                                                   Fp8Rows (&buf)[F8_NBUF]) {
   constexpr int HI = 32 * HB;
   auto uni = [](int64_t x) {
     return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
@@ -327,15 +330,22 @@ __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  i32x8 a[HB][2];
-  float wr[HB][16];
+  i32x8 a[NQ][HB][2];
+  float wr[NQ][HB][16];
+  int64_t s_q[NQ];                               // store bound of each query
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const uint8_t* qr = q_idx + ((int64_t)t * HI + hb * 32 + col) * D + 64 * half;
-    a[hb][0] = *(const i32x8*)qr;
-    a[hb][1] = *(const i32x8*)(qr + 32);
+  for (int j = 0; j < NQ; ++j) {
+    const int tj = t + (j < nvalid ? j : 0);
+    s_q[j] = j < nvalid ? uni(min(s_lim, p_first + j + 1)) : 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wr[hb][r] = w[(int64_t)t * HI + hb * 32 + mfma32_row(r, lane)];
+    for (int hb = 0; hb < HB; ++hb) {
+      const uint8_t* qr = q_idx + ((int64_t)tj * HI + hb * 32 + col) * D + 64 * half;
+      a[j][hb][0] = *(const i32x8*)qr;
+      a[j][hb][1] = *(const i32x8*)(qr + 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        wr[j][hb][r] = w[(int64_t)tj * HI + hb * 32 + mfma32_row(r, lane)];
+    }
   }
   const uint8_t* kb = k_idx + kb0 * D + 64 * half;
   auto load = [&](int64_t s0, Fp8Rows& dst) {
@@ -346,18 +356,21 @@ __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q
   };
   auto step = [&](int64_t s0, const Fp8Rows& rows) {
     const i32x8 k0 = cat8(rows.v[0], rows.v[1]), k1 = cat8(rows.v[2], rows.v[3]);
-    float v = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      f32x16 acc = mfma32x32x64_fp8(a[hb][0], k0, f32x16{});
-      acc = mfma32x32x64_fp8(a[hb][1], k1, acc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v = fmaf(wr[hb][r], relu(acc[r]), v);
-    }
-    v = halves_sum(v);
-    if constexpr (SCALED) v *= rows.sc;
     const int64_t s = s0 + col;
-    if (half == 0 && s < s_end) srow[s] = v;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x16 acc = mfma32x32x64_fp8(a[j][hb][0], k0, f32x16{});
+        acc = mfma32x32x64_fp8(a[j][hb][1], k1, acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaf(wr[j][hb][r], relu(acc[r]), v);
+      }
+      v = halves_sum(v);
+      if constexpr (SCALED) v *= rows.sc;
+      if (half == 0 && s < s_q[j]) scores[(int64_t)(t + j) * ld + s] = v;
+    }
   };
   if (s_beg >= s_end) return;
   if (!preloaded) {
@@ -374,8 +387,9 @@ __device__ __forceinline__ void decode_segment_fp8(const uint8_t* __restrict__ q
   }
 }
 
-// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = query offset j within its sequence.
-template <int HB, bool SCALED>
+// grid: x = flattened key rows / F8_KEYS_PER_BLOCK, y = group of NQ query offsets within its
+// sequence.
+template <int HB, bool SCALED, int NQ>
 __global__ __launch_bounds__(256) void indexer_decode_fp8(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const float* __restrict__ w,
@@ -410,14 +424,17 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8(
     if (kb1 <= f || kb0 > f) return f_end;
     const int64_t seg_end = min(f_end, kb1);
     const int nq = sp.q1 - sp.q0;
-    if (j < nq && sp.q0 + j < total_q && sp.q0 + j >= 0) {
-      const int t = sp.q0 + j;
-      const int64_t p = (kb1 - kb0) - nq + j;
+    const int j0 = j * NQ;
+    if (j0 < nq && sp.q0 + j0 >= 0 && sp.q0 + nq <= total_q) {
+      const int t = sp.q0 + j0;
+      const int nvalid = min(NQ, nq - j0);
+      const int64_t p_first = (kb1 - kb0) - nq + j0;
       const int64_t s_beg = f - kb0;
-      const int64_t s_end = min(min(seg_end - kb0, p + 1), ld);
-      decode_segment_fp8<HB, SCALED>(q_idx, k_idx, k_scale, w, t, kb0, s_beg + DEC_STEP * wave,
-                                     s_end, scores + (int64_t)t * ld, DEC_STEP * DEC_WAVES,
-                                     decltype(preloaded)::value, buf);
+      const int64_t s_lim = min(seg_end - kb0, ld);
+      const int64_t s_end = min(s_lim, p_first + nvalid);
+      decode_segment_fp8<HB, SCALED, NQ>(q_idx, k_idx, k_scale, w, t, nvalid, p_first, s_lim,
+                                         kb0, s_beg + DEC_STEP * wave, s_end, scores, ld,
+                                         DEC_STEP * DEC_WAVES, decltype(preloaded)::value, buf);
     }
     return seg_end;
   };
@@ -718,15 +735,24 @@ hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_i
                               float* scores, int64_t ld, hipStream_t stream) {
   const uint8_t* q = (const uint8_t*)q_idx;
   const uint8_t* k = (const uint8_t*)k_idx;
-  dim3 grid((unsigned)((b.total_k + F8_KEYS_PER_BLOCK - 1) / F8_KEYS_PER_BLOCK), b.max_q);
+  // as the bf16 kernel: up to four new tokens of a sequence share one key stream (32 heads)
+  const int nq = index_n_heads == 32 ? std::min(b.max_q, 4) : 1;
+  dim3 grid((unsigned)((b.total_k + F8_KEYS_PER_BLOCK - 1) / F8_KEYS_PER_BLOCK),
+            (unsigned)((b.max_q + nq - 1) / nq));
   auto go = [&](auto kern) {
     kern<<<grid, 256, 0, stream>>>(q, k, k_scale, w, b.cu_q, b.cu_k, b.nseq, b.total_q,
                                    b.total_k, scores, ld);
   };
-  if (index_n_heads == 32)
-    k_scale ? go(indexer_decode_fp8<1, true>) : go(indexer_decode_fp8<1, false>);
-  else
-    k_scale ? go(indexer_decode_fp8<2, true>) : go(indexer_decode_fp8<2, false>);
+  auto by_nq = [&](auto scaled) {
+    constexpr bool S = decltype(scaled)::value;
+    if (index_n_heads == 64) go(indexer_decode_fp8<2, S, 1>);
+    else if (nq == 1) go(indexer_decode_fp8<1, S, 1>);
+    else if (nq == 2) go(indexer_decode_fp8<1, S, 2>);
+    else if (nq == 3) go(indexer_decode_fp8<1, S, 3>);
+    else go(indexer_decode_fp8<1, S, 4>);
+  };
+  if (k_scale) by_nq(std::true_type{});
+  else by_nq(std::false_type{});
   return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ def check_scores_and_topk(case, d, scores, idx, k_scale=None, rows=None):
         assert np.array_equal(idx[t].cpu().numpy().astype(np.int64), want), f"row {t} indices"
 
 
-@pytest.mark.parametrize("name", ["decode_b32_l16k", "indexshare_b8_l256k", "mixed_b16_l512_1m"])
+@pytest.mark.parametrize("name", ["decode_b32_l16k", "indexshare_b8_l256k", "mixed_b16_l512_1m",
+                                  "mtp_b32_l16k_q4_shared"])
 def test_fp8_indexer_workloads_all_rows(name):
     case = DI.CASES[name]
     say("case", case.name)
