@@ -57,15 +57,24 @@ def parse():
     return ap.parse_args()
 
 
-def step_bytes(case, ib=2):
-    """Algorithmic HBM bytes of one step: every key row of the indexer cache, the selected
-    latent rows, queries, outputs, indexer queries and weights (intermediates excluded); ib =
-    bytes per indexer element (2 for bf16, 1 for fp8)."""
+def _key_rows(case):
+    """Key rows the indexer must read: per sequence, the rows its last new query sees (the
+    new queries of one sequence share them)."""
     import dsa_inputs as DI
-    tot = 0
+    last = {}
+    for t, b, p, base in DI.query_rows(case):
+        last[b] = max(last.get(b, 0), p + 1)
+    return sum(last.values())
+
+
+def step_bytes(case, ib=2):
+    """Algorithmic HBM bytes of one step: the key rows of the indexer cache (each once per
+    sequence), the selected latent rows of every query, queries, outputs, indexer queries and
+    weights (intermediates excluded); ib = bytes per indexer element (2 for bf16, 1 for fp8)."""
+    import dsa_inputs as DI
+    tot = _key_rows(case) * case.index_head_dim * ib                        # k_I rows
     for t, b, p, base in DI.query_rows(case):
         n = p + 1
-        tot += n * case.index_head_dim * ib                                 # k_I rows
         tot += min(case.index_topk, n) * case.d_qk * 2 * case.layers        # gathered rows
         tot += case.n_heads * (case.d_qk + case.d_v) * 2 * case.layers      # q in, out
         tot += case.index_n_heads * (case.index_head_dim * ib + 4)          # q_I, w
@@ -73,11 +82,8 @@ def step_bytes(case, ib=2):
 
 
 def indexer_bytes(case, ib=2):
-    import dsa_inputs as DI
-    tot = 0
-    for t, b, p, base in DI.query_rows(case):
-        tot += (p + 1) * case.index_head_dim * ib + case.index_n_heads * (case.index_head_dim * ib + 4)
-    return tot
+    return (_key_rows(case) * case.index_head_dim * ib
+            + case.total_q * case.index_n_heads * (case.index_head_dim * ib + 4))
 
 
 def mla_bytes(case):

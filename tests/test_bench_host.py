@@ -17,10 +17,14 @@ import dsa_inputs as DI  # noqa: E402
 # Decode, 32 x 16384: k_I 32*16384*256 + rows 32*2048*1152 + q/out 32*64*(576+512)*2
 # + q_I/w 32*32*(256+4). IndexShare: one k_I stream and four layers of rows, q and out.
 # Mixed lengths: the k_I rows of every sequence, min(2048, L) rows each, q/out/q_I/w per query.
+# MTP, 32 x 16384 with 4 new tokens each: the k_I rows once per sequence (32*16384*256), rows,
+# q/out and q_I/w per token (128 tokens).
 @pytest.mark.parametrize("name,step,mla", [
     ("decode_b32_l16k", 214_437_888, 79_953_920),
     ("indexshare_b8_l256k", 616_891_392, 19_988_480),
     ("mixed_b16_l512_1m", 949_534_848, 33_706_624),
+    ("mtp_b32_l16k_q4", 32 * 16384 * 256 + 128 * (2048 * 1152 + 64 * 1088 * 2 + 32 * 260),
+     128 * (2048 * 1152 + 64 * 1088 * 2)),
 ])
 def test_step_bytes(name, step, mla):
     case = DI.CASES[name]
@@ -32,6 +36,12 @@ def test_decode_bytes_closed_form():
     b, L, k = 32, 16384, 2048
     want = b * L * 128 * 2 + b * k * 576 * 2 + b * 64 * (576 + 512) * 2 + b * 32 * (128 * 2 + 4)
     assert bench.step_bytes(DI.CASES["decode_b32_l16k"]) == want
+
+
+def test_prefill_key_rows_counted_once():
+    """The chunk's 8192 queries share one key stream: 65536 rows of 256 B, not one per query."""
+    case = DI.CASES["prefill_chunk8k_l64k"]
+    assert bench.indexer_bytes(case) == 65536 * 256 + 8192 * 32 * 260
 
 
 def test_prefill_flops():
