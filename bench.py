@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 
 
@@ -442,13 +443,16 @@ def main():
     # the profile whose traffic record applies: workload, indexer dtype, selection kind
     prof = (args.workload + ("_fp8" if fp8 else "")
             + (f"_block{args.block_size}_{args.pool}" if blk else ""))
-    if max(case.seqlens_q) > 1 and case.dtype == torch.bfloat16:
-        # prefill: many queries share each key row, so the calls are matrix-core bound
-        dflops = indexer_flops(case) if dom == "indexer" else mla_flops(case)
+    # the bound of the dominant call from its arithmetic intensity against the ridge point:
+    # prefill's indexer (many queries per key row) is matrix-core bound, a few queries per
+    # sequence (decode, MTP) leave both calls memory bound
+    dflops = indexer_flops(case) if dom == "indexer" else mla_flops(case)
+    mpeak = FP8_PEAK_TFLOPS if (dom == "indexer" and fp8) else BF16_PEAK_TFLOPS
+    if case.dtype == torch.bfloat16 and dflops / dbytes > mpeak * 1e3 / HBM_PEAK_GBPS:
         achieved = dflops / (dms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "peak": mpeak, "unit": "TFLOP/s",
+                "frac": round(achieved / mpeak, 4),
                 "traffic": traffic_record(prof, dom), "traffic_unit": "B/launch",
                 "algorithmic_flops_per_launch": dflops, "avg_launch_ms": round(dms, 5)}
     else:
