@@ -107,6 +107,7 @@ def test_fp8_indexer_key_scales():
     ((37, 3000, 5, 9000, 65), (1, 2, 1, 3, 4), 32),
     ((300, 129), (40, 17), 32),            # many queries per sequence
     ((5000, 700, 12000), (1, 1, 2), 64),   # 64 indexer heads
+    ((9000, 7, 3000, 20000), (7, 7, 5, 15), 32),   # token groups of four, partial last groups
 ])
 def test_fp8_indexer_edge_cases(lens, nq, heads):
     name = f"fp8_edge_{lens}_{nq}_{heads}"

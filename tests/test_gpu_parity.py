@@ -381,6 +381,9 @@ def _small_case(name, seqlens_k, seqlens_q, **kw):
     ((4100,), (4100,), 2048),                # whole-sequence prefill
     ((9000,), (1,), 4096),                   # one query, 32 splits of two tiles each
     ((5000, 7000), (1, 1), 3000),            # k not a multiple of the 64-row tile, 24 splits
+    # several new tokens per sequence on one key stream: groups of four, a partial last group
+    ((9000, 7, 3000, 20000, 12), (7, 7, 5, 15, 1), 2048),
+    ((2050, 4, 6000), (4, 4, 3), 2048),       # tokens near the dense threshold, nq == L
 ])
 def test_ragged_edge_cases(lens, nq, k):
     case = _small_case(f"edge_{lens}_{nq}_{k}", lens, nq, index_topk=k)
