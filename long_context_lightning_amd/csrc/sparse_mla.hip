@@ -8,7 +8,8 @@
 // halves compute on the same gathered tile.
 //   * Tiles of 64 selected rows are gathered straight from HBM into LDS with direct
 //     global->LDS 16-byte loads, double-buffered: the gathers of tile i+1 go out during tile
-//     i's QK^T (once the barrier that ended tile i-1 has freed their stage) and land while
+//     i's QK^T (once the barrier that ended tile i-1, or for tile 0 the one after the query
+//     block was read out of stage 1, has freed their stage) and land while
 //     tile i computes; at the end of tile i each wave waits for its own gathers and one barrier
 //     publishes tile i+1 to the workgroup. Each row's 72 chunks of 16 B are stored with the
 //     chunk slot XOR-ed by a 3-bit function of the row (swz) that keeps every MFMA operand read
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
       // groups reads heads 0..31 again), and each wave reads its B operands from there with
       // the same conflict-free pattern as the QK A operands. It goes out first and tile 0
       // right behind it; loads complete in issue order, so the query block is read into
-      // registers while tile 0 still streams in, and tile 1 follows into stage 1 at once.
+      // registers while tile 0 still streams in.
       {
         int tt = tid;
         opaque(tt);
@@ -533,13 +534,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         for (int i = 0; i < QK_STEPS; ++i) asm volatile("" : "+v"(qreg[i]));
       }
       __syncthreads();
-      // tile 1 streams in while tile 0 lands and computes
-      if (1 < ntiles) {
-        issue(stage1, 1, i_odd);
-        wait_vmcnt<LOADS_PER_THREAD>();        // tile 0 (tile 1 may still be in flight)
-      } else {
-        wait_all_memory();
-      }
+      // Tile 1 goes out during tile 0's QK^T like every later tile, not here: issued behind
+      // tile 0 it shares the HBM queue with it and delays the first tile, and its stage could
+      // not take tile 2 before tile 0 ends anyway (measured: 2-5% faster per call).
+      wait_all_memory();
       __syncthreads();                         // tile 0 published
     }
 
@@ -622,7 +620,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
         auto rd = [&](int i, int b) __attribute__((always_inline)) { a[b] = *(const bf16x8*)(stage + abase[i & 3] + (i >> 2) * 128); };
         static_assert(2 * LOADS_PER_THREAD == QK_STEPS, "one gather per two QK steps");
         rd(0, 0);
-        if (tile >= 1 && tile + 1 < ntiles) {    // uniform
+        if (tile + 1 < ntiles) {    // uniform
           const int idxv = masked(tile + 1, idx_next);
           // the index of each gather's tile row, read across lanes (lane r holds row r's)
           int vsel[LOADS_PER_THREAD];
@@ -757,17 +755,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   }
 
   // ---- epilogue: 1/l per head, normalised output (final or partial) and log-sum-exp
-  // [0,256): each wave's share of the sum per head ([w4][64 heads]), [256,320): max per head,
-  // [320,384): sum per head
+  // fin [w4][64 heads]: each wave's share of the softmax sum per head; every lane then adds the
+  // four shares of its own head. After the tiles no barrier is needed before fin is written (the
+  // last tile's barrier ended every read of rbuf); without tiles the sequence lookup's reads of
+  // rbuf are still to be ordered.
   float* fin = (float*)rbuf;
-  __syncthreads();
+  if (ntiles == 0) __syncthreads();
   if (half == 0) fin[w4 * WG_HEADS + hl * HG + c32] = l_part;
-  if (w4 == 0 && half == 0) fin[4 * WG_HEADS + hl * HG + c32] = hl ? mref1 : mref0;
   __syncthreads();
-  if (tid < WG_HEADS)
-    fin[5 * WG_HEADS + tid] = (fin[tid] + fin[WG_HEADS + tid]) +
-                              (fin[2 * WG_HEADS + tid] + fin[3 * WG_HEADS + tid]);
-  __syncthreads();
+  const int hh = hl * HG + c32;
+  const float l_sum =
+      (fin[hh] + fin[WG_HEADS + hh]) + (fin[2 * WG_HEADS + hh] + fin[3 * WG_HEADS + hh]);
   // Every value a lane holds belongs to head (hl, c32): element r of value block db is column
   // 32*(VB_WAVE*cq + db) + 8*(r/4) + 4*half + r%4, so each group of four elements is four
   // consecutive columns of the head's output row. The normalised [64 heads x 512] block is
@@ -778,7 +776,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   {
     constexpr int OT_PITCH = DV * 2 + 16;
     static_assert(WG_HEADS * OT_PITCH <= STAGE_BYTES, "the staged block fits one stage");
-    const float l = fin[5 * WG_HEADS + hl * HG + c32];
+    const float l = l_sum;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     char* orow_lds = stage0 + (hl * HG + c32) * OT_PITCH + (VB_WAVE * cq * 32 + 4 * half) * 2;
 #pragma unroll
@@ -801,8 +799,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     }
   }
   if (w4 == 0 && half == 0 && heads_valid) {
-    const float l = fin[5 * WG_HEADS + hl * HG + c32];
-    const float val = l > 0.f ? (fin[4 * WG_HEADS + hl * HG + c32] + log2f(l)) * kLn2 : -INFINITY;
+    // the reference maxima are uniform across the workgroup
+    const float l = l_sum;
+    const float val = l > 0.f ? ((hl ? mref1 : mref0) + log2f(l)) * kLn2 : -INFINITY;
     const int64_t h = g32 * HG + c32;
     if (nsplit == 1) {
       if (lse) lse[(int64_t)t * H + h] = val;
