@@ -39,6 +39,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 namespace {
@@ -122,195 +123,50 @@ __device__ __forceinline__ int kept_elem(int q, int kh) { return 8 * (q >> 2) + 
 
 // ---------------------------------------------------------------------------------------------
 // Fused selection (decode rows of at most FUSED_MAX_POS positions): every workgroup of a query
-// computes the query's top-k threshold from its score row and writes its own split's slice of
-// the index row, so the top-k needs no launch of its own. The selection rule is step 2's: the k
-// largest scores among positions 0..p (compared as reals, an equal score going to the lower
-// position), every position when p + 1 <= k, ascending. Thread i holds `per` consecutive
-// positions (8, 16 or 32, as the row bound needs) as order-preserving keys (0 marks a position
-// past the row).
-//   rounds: three radix digits of the key (bits 31..21, 20..10, 9..0), each counted in a
-//           2048-bin LDS histogram over the keys that share the digits found so far, give the
-//           threshold key (the k-th largest) and how many positions holding it are taken. Each
-//           round takes one barrier: its histogram was cleared in an earlier phase, and every
-//           wave finds the bin by itself (lane l sums 32 bins, a wave prefix sum picks the lane,
-//           then each lane takes one of that lane's bins and a second prefix sum picks the bin);
-//   ranks:  each thread's taken positions as a bit mask (scores at least the threshold; when
-//           ties at the threshold are not all taken, the extra equal ones are cleared from the
-//           highest positions down); a workgroup prefix sum of the mask populations gives each
-//           thread the rank of its first taken position, and only the bits whose ranks fall in
-//           the split's slice are written out.
+// computes the query's top-k from its score row with the workgroup select of select.hpp (thread
+// i holds `per` consecutive positions, 8, 16 or 32 as the row bound needs) and writes only its
+// own split's slice of the index row, so the top-k needs no launch of its own. The rule is step
+// 2's: the k largest scores among positions 0..p, an equal score going to the lower position,
+// every position when p + 1 <= k, ascending.
 // ---------------------------------------------------------------------------------------------
 constexpr int FUSED_PER = 32;                                 // positions per thread, at most
 constexpr int FUSED_MAX_POS = FUSED_PER * NTHREADS;            // 16384
-constexpr int SEL_BINS = 2048;
-// bin b is stored at word b + b / 32 (one pad word after every 32 bins, so that lane l reading
-// the i-th bin of group l meets no other lane's bank), followed by one dummy bin per lane
-constexpr int SEL_PADDED = SEL_BINS + SEL_BINS / 32;
-constexpr int SEL_HIST = SEL_PADDED + WAVE;
-__device__ __forceinline__ uint32_t sel_slot(uint32_t b) { return b + (b >> 5); }
 constexpr int SEL_LIST = 2048;                 // longest slice of one split
-constexpr int SEL_H1 = SEL_HIST;                              // round 1's histogram
-constexpr int SEL_H2 = 2 * SEL_HIST;                          // round 2's
-constexpr int SEL_LIST_AT = 3 * SEL_HIST;
-constexpr int SEL_SCRATCH_WORDS = SEL_LIST_AT + SEL_LIST + 2 * NWAVES;
+constexpr int SEL_LIST_AT = sel_scratch_words<NTHREADS>();
+constexpr int SEL_SCRATCH_WORDS = SEL_LIST_AT + SEL_LIST;
 static_assert(SEL_SCRATCH_WORDS * 4 <= STAGE_BYTES, "fused selection scratch must fit one stage");
 
-// Loads this thread's PER scores of the row, positions PER*tid .. PER*tid + PER - 1 (positions
-// past `lim` are left at 0 and masked later).
-template <int PER>
-__device__ __forceinline__ void fused_load_scores(const float* __restrict__ srow, int64_t lim,
-                                                  bool aligned, float (&v)[PER]) {
-  const int64_t p0 = (int64_t)threadIdx.x * PER;
-  if (aligned && p0 + PER <= lim) {
-#pragma unroll
-    for (int i = 0; i < PER / 4; ++i) {
-      const f32x4 x = *(const f32x4*)(srow + p0 + 4 * i);
-      v[4 * i] = x[0]; v[4 * i + 1] = x[1]; v[4 * i + 2] = x[2]; v[4 * i + 3] = x[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = p0 + i < lim ? srow[p0 + i] : 0.f;
-  }
-}
-
-// Searches bins 0..2047 (bin b at word sel_slot(b)) from the top for the one holding the need-th
-// largest key; every wave does it by itself and gets the same (bin, keys still needed inside
-// it). Subtractions are written so that none is guarded by a comparison: the compiler marks a
-// guarded one wrap-free, hoists it and then folds comparisons and minima with its operands away.
-__device__ __forceinline__ void fused_find_bin(const uint32_t* __restrict__ hc, uint32_t need,
-                                               uint32_t& bin, uint32_t& rem) {
-  const int lane = lane_id();
-  const int g = WAVE - 1 - lane;                         // this lane's bins 32g .. 32g + 31
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) sum += hc[33 * g + i];
-  const uint32_t above = wave_incl_scan_u32(sum) - sum;  // keys in the bins of lower lanes
-  const uint64_t hit = __ballot(above < need && above + sum >= need);
-  const int fl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
-  const uint32_t above_fl = __builtin_amdgcn_readlane(above, fl);
-  // lane j (< 32) takes bin top - j of lane fl's 32 bins
-  const int gf = WAVE - 1 - fl;
-  const uint32_t h = lane < 32 ? hc[33 * gf + 31 - lane] : 0u;
-  const uint32_t cum = above_fl + wave_incl_scan_u32(h) - h;
-  const uint64_t hit2 = __ballot(cum < need && cum + h >= need);
-  const int j = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit2));
-  bin = (uint32_t)(32 * gf + 31 - j);
-  rem = need - min(__builtin_amdgcn_readlane(cum, j), need);
-}
-
-// Clears the histograms of rounds 0 and 1 in the fused selection's scratch (before a barrier
-// that precedes fused_select_slice).
-__device__ __forceinline__ void fused_clear(uint32_t* __restrict__ scratch) {
-  for (int i = threadIdx.x; i < SEL_H2; i += NTHREADS) scratch[i] = 0;
-}
-
 // Writes idx_row[r] for r in [r_beg, r_end) (r_end - r_beg <= SEL_LIST) from the scores v of
-// positions 0..n-1 (fused_load_scores). scratch: SEL_SCRATCH_WORDS words of LDS whose first two
-// histograms fused_clear zeroed before a barrier. Every thread of the workgroup calls it.
+// positions 0..n-1 (sel_load_scores). scratch: SEL_SCRATCH_WORDS words of LDS whose first two
+// histograms were zeroed before a barrier. Every thread of the workgroup calls it.
 template <int PER>
 __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_t n, int k,
                                                    int r_beg, int r_end, int32_t* idx_row,
                                                    uint32_t* __restrict__ scratch) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = lane_id();
   uint32_t* list = scratch + SEL_LIST_AT;      // [SEL_LIST] the split's slice
-  uint32_t* red = list + SEL_LIST;             // [2][NWAVES] prefix-sum partials
   if (n <= k) {                                // dense: every visible position
     for (int r = r_beg + tid; r < r_end; r += NTHREADS) idx_row[r] = r < n ? r : -1;
     return;
   }
-  const int64_t p0 = (int64_t)tid * PER;
   uint32_t key[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = p0 + i < n ? score_key(v[i]) : 0u;  // never 0
-  // round 0: bits 31..21 of every key (a position past the row counts in its lane's dummy bin)
-  uint32_t need = (uint32_t)k, bin;
-  {
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      atomicAdd(&scratch[key[i] ? sel_slot(key[i] >> 21) : SEL_PADDED + lane], 1u);
-    __syncthreads();
-    fused_find_bin(scratch, need, bin, need);
-  }
-  uint32_t pref = bin;                         // bits 31..21 of the threshold
-  // round 1: bits 20..10 of the keys sharing them (H1; H2 is cleared meanwhile)
-  {
-    uint32_t* hc = scratch + SEL_H1;
-    for (int i = tid; i < SEL_HIST; i += NTHREADS) scratch[SEL_H2 + i] = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if ((key[i] >> 21) == pref) atomicAdd(&hc[sel_slot((key[i] >> 10) & 2047u)], 1u);
-    __syncthreads();
-    fused_find_bin(hc, need, bin, need);
-  }
-  pref = (pref << 11) | bin;                   // bits 31..10
-  // round 2: bits 9..0 (H2; bins 1024.. stay empty)
-  {
-    uint32_t* hc = scratch + SEL_H2;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if ((key[i] >> 10) == pref) atomicAdd(&hc[sel_slot(key[i] & 1023u)], 1u);
-    __syncthreads();
-    fused_find_bin(hc, need, bin, need);
-  }
-  const uint32_t lo = (pref << 10) | bin;
-  const uint32_t thr = lo;                     // the k-th largest key; `need` positions holding it
-  uint32_t ge = 0;                             // are taken
-#pragma unroll
-  for (int i = 0; i < PER; ++i) ge |= (key[i] >= thr ? 1u : 0u) << i;
-  uint32_t cnt = __popc(ge);
-  uint32_t incl = wave_incl_scan_u32(cnt);
-  if (lane == WAVE - 1) red[wave] = incl;
+  sel_keys(v, n, key);
+  sel_count0(key, scratch);
   __syncthreads();
-  uint32_t before = incl - cnt, total = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVES; ++w) {
-    const uint32_t x = red[w];
-    before += w < wave ? x : 0u;
-    total += x;
-  }
-  if (total > (uint32_t)k) {                   // uniform: ties at the threshold not all taken
-    // the taken equal keys are the first `need` in position order: drop this thread's last
-    // (its equal keys past the need-th) from the mask
-    uint32_t eq = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) eq |= (key[i] == thr ? 1u : 0u) << i;
-    const uint32_t n_eq = __popc(eq);
-    const uint32_t e_incl = wave_incl_scan_u32(n_eq);
-    if (lane == WAVE - 1) red[NWAVES + wave] = e_incl;
-    __syncthreads();
-    uint32_t e_before = e_incl - n_eq;
-#pragma unroll
-    for (int w = 0; w < NWAVES; ++w) e_before += w < wave ? red[NWAVES + w] : 0u;
-    const uint32_t e_taken_before = min(e_before, need);
-    uint32_t drop = n_eq - min(n_eq, need - e_taken_before);
-    while (drop > 0) {                         // clear the highest equal positions
-      const uint32_t top = 1u << (31 - __builtin_clz(eq));
-      eq ^= top;
-      ge ^= top;
-      --drop;
-    }
-    // ranks: keys above the threshold before this thread, plus the equal ones taken before it
-    uint32_t gt_cnt = __popc(ge) - min(n_eq, need - e_taken_before);
-    const uint32_t g_incl = wave_incl_scan_u32(gt_cnt);
-    if (lane == WAVE - 1) red[wave] = g_incl;  // (every wave read red[0..7] before the barrier
-    __syncthreads();                           //  above)
-    before = g_incl - gt_cnt + e_taken_before;
-#pragma unroll
-    for (int w = 0; w < NWAVES; ++w) before += w < wave ? red[w] : 0u;
-  }
-  // write the taken positions whose ranks fall in [r_beg, r_end)
-  uint32_t rk = before;
-  uint32_t m = ge;
-  // skip the taken positions ranked before r_beg
-  uint32_t skip = min((uint32_t)r_beg - min(rk, (uint32_t)r_beg), (uint32_t)__popc(m));
+  const SelThreshold s = sel_threshold<NTHREADS, PER>(key, (uint32_t)k, scratch);
+  typename SelMask<PER>::T m;
+  uint32_t rk;
+  sel_ranks<NTHREADS, PER>(key, s, (uint32_t)k, scratch + SEL_RED, m, rk);
+  // write the taken positions whose ranks fall in [r_beg, r_end), skipping those ranked before
+  // r_beg
+  uint32_t skip = min((uint32_t)r_beg - min(rk, (uint32_t)r_beg), (uint32_t)sel_popc(m));
   rk += skip;
   while (skip > 0) {
     m &= m - 1;
     --skip;
   }
   while (m != 0 && rk < (uint32_t)r_end) {
-    const int i = __builtin_ctz(m);
+    const int i = sel_low_index(m);
     list[rk - r_beg] = (uint32_t)(tid * PER + i);
     m &= m - 1;
     ++rk;
@@ -383,9 +239,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   // starts at once and reads the same few cache lines of cu_seqlens.
   float fs[FUSED ? FPER : 1];                           // this thread's scores (FUSED)
   if constexpr (FUSED)                                  // issued before the sequence lookup
-    fused_load_scores<FPER>(scores + (int64_t)t * ld_scores,
+    sel_load_scores<FPER>(scores + (int64_t)t * ld_scores,
                             min(ld_scores, (int64_t)FUSED_MAX_POS), (ld_scores & 3) == 0, fs);
-  if constexpr (FUSED) fused_clear((uint32_t*)stage0);   // (ordered by the lookup's barrier)
+  if constexpr (FUSED) sel_clear<NTHREADS>((uint32_t*)stage0, 2);   // (ordered by the lookup's barrier)
   QueryPos qp;
   {
     int64_t* qs = (int64_t*)rbuf;
