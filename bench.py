@@ -136,11 +136,13 @@ def traffic_record(workload, kernel):
     if rec is None:
         return None
     csrc = os.path.join(ROOT, "long_context_lightning_amd", "csrc")
-    for name, sha in rec.get("code_sha256", {}).items():
+    shas = rec.get("code_sha256")
+    # every kernel source of the tree, and only those, with the digests the counters were taken at
+    if not shas or set(shas) != set(os.listdir(csrc)):
+        return None
+    for name, sha in shas.items():
         if code_digest(os.path.join(csrc, name)) != sha:
             return None
-    if "code_sha256" not in rec:
-        return None
     key = "traffic_bytes_per_launch" if kernel == rec["kernel"] else f"{kernel}_traffic_bytes_per_launch"
     return rec.get(key)
 

@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU): its algorithmic byte and FLOP counts against the
 per-step figures worked out independently from the workload shapes, and its refusal of more
 than one GPU."""
+import json
 import os
 import subprocess
 import sys
@@ -57,3 +58,32 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_record_needs_every_current_source(tmp_path, monkeypatch):
+    """A traffic record counts only while it lists every kernel source of the tree with the
+    digest the counters were taken at: a changed, added or missing source voids it."""
+    csrc = tmp_path / "long_context_lightning_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "a.hip").write_text("int a;  // comment\n")
+    (csrc / "b.hpp").write_text("int b;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+
+    def write(shas):
+        rec = {"code_sha256": shas, "kernel": "sparse_mla", "traffic_bytes_per_launch": 123}
+        (tmp_path / "profiles" / "w_hbm_traffic.md").write_text("traffic-record: " + json.dumps(rec) + "\n")
+
+    good = {n: bench.code_digest(str(csrc / n)) for n in ("a.hip", "b.hpp")}
+    write(good)
+    assert bench.traffic_record("w", "sparse_mla") == 123
+    (csrc / "a.hip").write_text("int a;  // another comment\n")          # comments only
+    assert bench.traffic_record("w", "sparse_mla") == 123
+    write({"a.hip": good["a.hip"]})                                      # b.hpp not covered
+    assert bench.traffic_record("w", "sparse_mla") is None
+    write(good)
+    (csrc / "c.hpp").write_text("int c;\n")                              # a source added
+    assert bench.traffic_record("w", "sparse_mla") is None
+    (csrc / "c.hpp").unlink()
+    (csrc / "b.hpp").write_text("int b2;\n")                             # code changed
+    assert bench.traffic_record("w", "sparse_mla") is None
