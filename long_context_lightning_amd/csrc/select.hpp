@@ -1,6 +1,6 @@
 // Exact top-k of the keys one workgroup holds: the threshold by three radix rounds in LDS, then
 // the rank of every taken key in position order. Used by the selection inside the sparse-MLA
-// launch and by the chunked top-k of long rows.
+// launch.
 //
 // Selection rule of step 2 ("How GLM5.3 Sparse Attention Affects HBM Memory Usage", How it works
 // / Model): the k largest scores, compared as reals, an equal score going to the lower position.
@@ -12,12 +12,12 @@
 //           threshold key (the k-th largest) and how many keys equal to it are taken. Every wave
 //           finds the bin by itself (lane l sums 32 bins, a wave prefix sum picks the lane, then
 //           each lane takes one of that lane's bins and a second prefix sum picks the bin), so a
-//           round costs one barrier. Round 0's histogram is either counted here or handed in
-//           (the chunked top-k sums the per-chunk histograms instead);
-//   ranks:  each thread's taken keys as a bit mask (keys at least the threshold; when the keys
-//           equal to it are not all taken, the extra ones are cleared from the highest positions
-//           down); a workgroup prefix sum of the mask populations gives each thread the rank of
-//           its first taken key.
+//           round costs one barrier (round 0's histogram is counted by sel_count0 before the
+//           barrier that precedes sel_threshold);
+//   ranks:  each thread's taken keys as a bit mask (keys above the threshold, and of the keys
+//           equal to it the first ones in position order, as many as are taken); workgroup
+//           prefix sums of the counts above and equal give each thread the rank of its first
+//           taken key.
 // Subtractions are written so that none is guarded by a comparison (n - min(x, n), never
 // x >= n ? 0 : n - x): the compiler marks a guarded one wrap-free, hoists it, and then folds
 // comparisons and minima of its operands away.
@@ -161,64 +161,47 @@ __device__ __forceinline__ SelThreshold sel_threshold(const uint32_t (&key)[PER]
   return r;
 }
 
-// This thread's taken keys (exactly k over the workgroup) as a mask over its PER keys, and the
-// rank in position order of its first taken key. red: 2 * waves words of scratch that no other
-// code reads meanwhile. One barrier; three when the keys equal to the threshold are not all
-// taken.
+// This thread's taken keys (exactly the k of sel_threshold over the workgroup) as a mask over its
+// PER keys, and the rank in position order of its first taken key: every key above the
+// threshold, and the first s.need keys equal to it in position order (the count of keys above it
+// is k - s.need). The counts above and equal meet in one exchange of wave totals. red: 2 * waves
+// words of scratch that no other code reads meanwhile. One barrier.
 template <int THREADS, int PER>
 __device__ __forceinline__ void sel_ranks(const uint32_t (&key)[PER], const SelThreshold& s,
-                                          uint32_t k, uint32_t* __restrict__ red,
+                                          uint32_t* __restrict__ red,
                                           typename SelMask<PER>::T& taken, uint32_t& before) {
   typedef typename SelMask<PER>::T M;
   constexpr int NW = THREADS / WAVE;
   const int wave = threadIdx.x / WAVE, lane = lane_id();
   const uint32_t thr = s.thr, need = s.need;
-  M ge = 0;
+  M gt = 0, eq = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) ge |= (key[i] >= thr ? (M)1 : (M)0) << i;
-  const uint32_t cnt = sel_popc(ge);
-  const uint32_t incl = wave_incl_scan_u32(cnt);
-  if (lane == WAVE - 1) red[wave] = incl;
+  for (int i = 0; i < PER; ++i) {
+    gt |= (key[i] > thr ? (M)1 : (M)0) << i;
+    eq |= (key[i] == thr ? (M)1 : (M)0) << i;
+  }
+  const uint32_t cg = sel_popc(gt), ce = sel_popc(eq);
+  const uint32_t ig = wave_incl_scan_u32(cg), ie = wave_incl_scan_u32(ce);
+  if (lane == WAVE - 1) {
+    red[wave] = ig;
+    red[NW + wave] = ie;
+  }
   __syncthreads();
-  before = incl - cnt;
-  uint32_t total = 0;
+  uint32_t g_before = ig - cg, e_before = ie - ce;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const uint32_t x = red[w];
-    before += w < wave ? x : 0u;
-    total += x;
+    g_before += w < wave ? red[w] : 0u;
+    e_before += w < wave ? red[NW + w] : 0u;
   }
-  if (total > k) {                             // uniform: keys equal to thr not all taken
-    // the taken equal keys are the first `need` in position order: drop this thread's last
-    // (its equal keys past the need-th) from the mask
-    M eq = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) eq |= (key[i] == thr ? (M)1 : (M)0) << i;
-    const uint32_t n_eq = sel_popc(eq);
-    const uint32_t e_incl = wave_incl_scan_u32(n_eq);
-    if (lane == WAVE - 1) red[NW + wave] = e_incl;
-    __syncthreads();
-    uint32_t e_before = e_incl - n_eq;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) e_before += w < wave ? red[NW + w] : 0u;
-    const uint32_t e_taken_before = min(e_before, need);
-    uint32_t drop = n_eq - min(n_eq, need - e_taken_before);
-    while (drop > 0) {                         // clear the highest equal positions
-      const M top = sel_top_bit(eq);
-      eq ^= top;
-      ge ^= top;
-      --drop;
-    }
-    // ranks: keys above the threshold before this thread, plus the equal ones taken before it
-    const uint32_t gt_cnt = sel_popc(ge) - min(n_eq, need - e_taken_before);
-    const uint32_t g_incl = wave_incl_scan_u32(gt_cnt);
-    if (lane == WAVE - 1) red[wave] = g_incl;  // (every wave read red[0..NW) before the barrier
-    __syncthreads();                           //  above)
-    before = g_incl - gt_cnt + e_taken_before;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) before += w < wave ? red[w] : 0u;
+  // equal keys taken before this thread, and this thread's: its lowest positions
+  const uint32_t e_taken_before = min(e_before, need);
+  uint32_t drop = ce - min(ce, need - e_taken_before);
+  while (drop > 0) {                           // clear the highest equal positions
+    eq ^= sel_top_bit(eq);
+    --drop;
   }
-  taken = ge;
+  taken = gt | eq;
+  before = g_before + e_taken_before;
 }
 
 }  // namespace dsa

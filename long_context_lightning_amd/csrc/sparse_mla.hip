@@ -156,7 +156,7 @@ __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_
   const SelThreshold s = sel_threshold<NTHREADS, PER>(key, (uint32_t)k, scratch);
   typename SelMask<PER>::T m;
   uint32_t rk;
-  sel_ranks<NTHREADS, PER>(key, s, (uint32_t)k, scratch + SEL_RED, m, rk);
+  sel_ranks<NTHREADS, PER>(key, s, scratch + SEL_RED, m, rk);
   // write the taken positions whose ranks fall in [r_beg, r_end), skipping those ranked before
   // r_beg
   uint32_t skip = min((uint32_t)r_beg - min(rk, (uint32_t)r_beg), (uint32_t)sel_popc(m));
