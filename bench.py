@@ -68,16 +68,17 @@ def _key_rows(case):
     return sum(last.values())
 
 
-def step_bytes(case, ib=2):
+def step_bytes(case, ib=2, ab=2):
     """Algorithmic HBM bytes of one step: the key rows of the indexer cache (each once per
     sequence), the selected latent rows of every query, queries, outputs, indexer queries and
-    weights (intermediates excluded); ib = bytes per indexer element (2 for bf16, 1 for fp8)."""
+    weights (intermediates excluded); ib = bytes per indexer element (2 for bf16, 1 for fp8,
+    4 for fp32), ab = bytes per attention element (2 for bf16, 4 for fp32)."""
     import dsa_inputs as DI
     tot = _key_rows(case) * case.index_head_dim * ib                        # k_I rows
     for t, b, p, base in DI.query_rows(case):
         n = p + 1
-        tot += min(case.index_topk, n) * case.d_qk * 2 * case.layers        # gathered rows
-        tot += case.n_heads * (case.d_qk + case.d_v) * 2 * case.layers      # q in, out
+        tot += min(case.index_topk, n) * case.d_qk * ab * case.layers       # gathered rows
+        tot += case.n_heads * (case.d_qk + case.d_v) * ab * case.layers     # q in, out
         tot += case.index_n_heads * (case.index_head_dim * ib + 4)          # q_I, w
     return tot
 
@@ -87,11 +88,12 @@ def indexer_bytes(case, ib=2):
             + case.total_q * case.index_n_heads * (case.index_head_dim * ib + 4))
 
 
-def mla_bytes(case):
+def mla_bytes(case, ab=2):
     import dsa_inputs as DI
     tot = 0
     for t, b, p, base in DI.query_rows(case):
-        tot += min(case.index_topk, p + 1) * case.d_qk * 2 + case.n_heads * (case.d_qk + case.d_v) * 2
+        tot += (min(case.index_topk, p + 1) * case.d_qk * ab
+                + case.n_heads * (case.d_qk + case.d_v) * ab)
     return tot
 
 
@@ -224,7 +226,13 @@ def main():
     # selected latent rows). Between two uses of one set the other sets touch at least 1 GiB,
     # four times the Infinity Cache, so no step is served from an earlier step's cached lines.
     fp8 = args.index_dtype == "fp8"
-    touched = step_bytes(case, 1 if fp8 else 2)
+    f32 = case.dtype == torch.float32
+    if fp8 and f32:
+        sys.exit("bench.py: the fp8 indexer runs on the bf16 path; this workload is fp32")
+    dt = 0 if f32 else 1                     # dsa_dtype of q, kv, out (and q_I, k_I unless fp8)
+    ab = 4 if f32 else 2                     # bytes per attention element
+    eb = 1 if fp8 else ab                    # bytes per indexer element
+    touched = step_bytes(case, eb, ab)
     nsets = args.sets or max(2, 1 + math.ceil((1 << 30) / touched))
     sets = []
     for i in range(nsets):
@@ -264,7 +272,7 @@ def main():
     fargs = [[dsa._CForwardArgs(d["q_idx"].data_ptr(), d["k_idx"].data_ptr(), d["w"].data_ptr(),
                                 case.index_n_heads, case.index_head_dim, case.index_topk,
                                 d["q"][l].data_ptr(), d["kv"][l].data_ptr(), case.n_heads,
-                                case.d_qk, case.d_v, case.softmax_scale, 1, 1 if fp8 else 0,
+                                case.d_qk, case.d_v, case.softmax_scale, dt, 1 if fp8 else 0,
                                 None, args.block_size if blk else 0, pool_code)
               for l in range(case.layers)] for d in sets]
 
@@ -286,7 +294,7 @@ def main():
                                             case.index_head_dim, scores.data_ptr(), ld, sp)
         return L.dsa_indexer_scores(batch.ptr, d["q_idx"].data_ptr(), d["k_idx"].data_ptr(),
                                     d["w"].data_ptr(), case.index_n_heads, case.index_head_dim,
-                                    1, scores.data_ptr(), ld, sp)
+                                    dt, scores.data_ptr(), ld, sp)
 
     def step(i, ev=None):
         step_on(i, sp, ev)
@@ -310,7 +318,7 @@ def main():
         for l in range(case.layers):       # IndexShare: the group's layers reuse the indices
             st |= L.dsa_sparse_mla_fwd(batch.ptr, d["q"][l].data_ptr(), d["kv"][l].data_ptr(),
                                        idx.data_ptr(), case.index_topk, case.n_heads, case.d_qk,
-                                       case.d_v, case.softmax_scale, 1, outs[l].data_ptr(),
+                                       case.d_v, case.softmax_scale, dt, outs[l].data_ptr(),
                                        lse.data_ptr(), ws.data_ptr(), ws.numel(), sp)
         if ev is not None:
             ev[3].record(stream)
@@ -425,7 +433,7 @@ def main():
         d, l = sets[i % nsets], i % case.layers
         return L.dsa_sparse_mla_fwd(batch.ptr, d["q"][l].data_ptr(), d["kv"][l].data_ptr(),
                                     idx.data_ptr(), case.index_topk, case.n_heads, case.d_qk,
-                                    case.d_v, case.softmax_scale, 1, outs[l].data_ptr(),
+                                    case.d_v, case.softmax_scale, dt, outs[l].data_ptr(),
                                     lse.data_ptr(), ws.data_ptr(), ws.numel(), sp)
 
     launch_ms = {"indexer": time_calls(idx_call), "sparse_mla": time_calls(mla_call)}
@@ -436,9 +444,8 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    eb = 1 if fp8 else 2
-    sb = step_bytes(case, eb)
-    ib, mb = indexer_bytes(case, eb), mla_bytes(case)          # one call = one layer
+    sb = step_bytes(case, eb, ab)
+    ib, mb = indexer_bytes(case, eb), mla_bytes(case, ab)      # one call = one layer
     kern = {"indexer": (launch_ms["indexer"], ib), "sparse_mla": (launch_ms["sparse_mla"], mb)}
     dom = max(kern, key=lambda k: kern[k][0])
     dms, dbytes = kern[dom]
