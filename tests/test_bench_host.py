@@ -87,3 +87,14 @@ def test_traffic_record_needs_every_current_source(tmp_path, monkeypatch):
     (csrc / "c.hpp").unlink()
     (csrc / "b.hpp").write_text("int b2;\n")                             # code changed
     assert bench.traffic_record("w", "sparse_mla") is None
+
+
+def test_fp32_workload_bytes():
+    """The tiny fp32 prefill (one sequence of 256 tokens, indexer 4 x 32, top-64, 8 heads over
+    80-wide rows with 64 value columns) counts 4-byte elements: key rows 256*32*4 = 32768;
+    gathered rows sum_t min(64, t+1) = 2080 + 192*64 = 14368 rows of 80*4 B = 4597760; queries
+    and outputs 256*8*(80+64)*4 = 1179648; q_I and w 256*4*(32*4+4) = 135168."""
+    case = DI.CASES["tiny_prefill_fp32"]
+    assert bench.step_bytes(case, 4, 4) == 32768 + 4597760 + 1179648 + 135168
+    assert bench.indexer_bytes(case, 4) == 32768 + 135168
+    assert bench.mla_bytes(case, 4) == 4597760 + 1179648
