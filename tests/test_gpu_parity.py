@@ -724,6 +724,7 @@ def test_split_partials_against_one_split():
     ((5000, 7000, 16384), (1, 1, 1), {"index_topk": 3000}),           # k not a multiple of 64
     ((16384, 6000), (1, 2), {"n_heads": 128}),                         # two head groups per split
     ((16384, 6000, 3333), (1, 1, 1), {"n_heads": 32}),
+    ((16385, 9000), (1, 1), {}),                   # one position past the in-launch bound
 ])
 def test_forward_fused_selection_matches_topk(lens, nq, kw):
     """dsa_forward on rows of at most 16384 positions selects the top-k inside the sparse-MLA
