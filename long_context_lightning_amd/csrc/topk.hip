@@ -83,32 +83,42 @@ struct TopkShared {
   int32_t cand_pos[TK_OBUF];
 };
 
-// Finds, in histogram h (bins 2*tid and 2*tid+1 per thread, keys counted from the top bin
-// down), the bin holding the need-th largest key, and publishes it with the keys still needed
-// from it, its count and its smallest and largest key. Two barriers; all threads must call.
+// Finds, in histogram h (bins BPT*tid .. BPT*tid + BPT - 1 per thread, BPT = TK_BINS / THREADS,
+// keys counted from the top bin down), the bin holding the need-th largest key, and publishes it
+// with the keys still needed from it, its count and its smallest and largest key. Two barriers;
+// all threads must call.
+template <int THREADS>
 __device__ __forceinline__ void select_bin(const uint32_t* h, const uint32_t* bmin,
                                            const uint32_t* bmax, uint32_t need,
                                            TopkShared& sh) {
+  constexpr int BPT = TK_BINS / THREADS;
+  static_assert(BPT * THREADS == TK_BINS, "whole bins per thread");
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const uint32_t h0 = h[2 * tid], h1 = h[2 * tid + 1];
-  const uint32_t incl = wave_incl_scan_u32(h0 + h1);
+  uint32_t hv[BPT];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    hv[j] = h[BPT * tid + j];
+    sum += hv[j];
+  }
+  const uint32_t incl = wave_incl_scan_u32(sum);
   const uint32_t wave_tot = last_lane(incl);
   if (lane_id() == 0) sh.red_a[wave] = wave_tot;
   __syncthreads();
-  uint32_t above = wave_tot - incl;            // keys in bins above this thread's two bins
+  uint32_t above = wave_tot - incl;            // keys in bins above this thread's bins
 #pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w)
+  for (int w = 0; w < THREADS / WAVE; ++w)
     if (w > wave) above += sh.red_a[w];
   int b = -1;
-  if (above < need && above + h1 >= need) {
-    b = 2 * tid + 1;
-    sh.sel_need = need - above;
-    sh.sel_count = h1;
-  } else if (above + h1 < need && above + h1 + h0 >= need) {
-    b = 2 * tid;
-    sh.sel_need = need - above - h1;
-    sh.sel_count = h0;
+#pragma unroll
+  for (int j = BPT - 1; j >= 0; --j) {         // this thread's bins from the top
+    if (b < 0 && above < need && above + hv[j] >= need) {
+      b = BPT * tid + j;
+      sh.sel_need = need - above;
+      sh.sel_count = hv[j];
+    }
+    above += hv[j];
   }
   if (b >= 0) {
     sh.sel_bin = b;
@@ -127,14 +137,14 @@ __device__ __forceinline__ uint32_t lin_bin(float x, float scale, float bias) {
 
 // MODE: 0 = every row fits one register chunk; 1 = longer rows streamed through the candidate
 // buffer (k <= TK_OBUF); 2 = longer rows re-read chunk by chunk on every pass.
-template <int UNITS, int MODE>
-__global__ __launch_bounds__(TK_THREADS) void topk_rows(
+template <int THREADS, int UNITS, int MODE>
+__global__ __launch_bounds__(THREADS, 4) void topk_rows(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int k,
     int32_t* __restrict__ out) {
   __shared__ TopkShared sh;
   constexpr int SLICE4 = UNITS * WAVE;           // 16-byte groups per wave and chunk
-  constexpr int CHUNK4 = UNITS * TK_THREADS;     // 16-byte groups per chunk
+  constexpr int CHUNK4 = UNITS * THREADS;     // 16-byte groups per chunk
   constexpr uint32_t ALL = 0xffffffffu;
 
   const int t = blockIdx.x;
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   const int64_t n = min(qp.p + 1, ld);           // visible positions 0..n-1 (0 if invalid)
   int32_t* orow = out + (int64_t)t * k;
   if (n <= k) {                                  // dense path: everything visible is selected
-    for (int i = tid; i < k; i += TK_THREADS) orow[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += THREADS) orow[i] = i < n ? i : -1;
     return;
   }
   const int ni = (int)n;
@@ -214,7 +224,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   // lowest positions, which is exactly the part of them the final selection can take. Thread i
   // holds candidates CPT*i.. in index order (NaN past the count). Otherwise every pass re-reads
   // the row chunk by chunk.
-  constexpr int CPT = TK_OBUF / TK_THREADS;
+  constexpr int CPT = TK_OBUF / THREADS;
   constexpr bool stream = MODE == 1;
   constexpr bool resident = MODE != 2;           // x holds the whole current segment
   float cv[CPT];
@@ -246,11 +256,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   // The threshold T of the current segment and how many scores equal to T are taken (all of
   // them when the result is ALL).
   auto select = [&](float& thr, uint32_t& thr_need) {
-    for (int i = tid; i < TK_HIST; i += TK_THREADS) {
+    for (int i = tid; i < TK_HIST; i += THREADS) {
       sh.hist[0][i] = 0;
       sh.hist[1][i] = 0;
     }
-    for (int i = tid; i < TK_BINS; i += TK_THREADS) {
+    for (int i = tid; i < TK_BINS; i += THREADS) {
       sh.bmin[0][i] = ALL;
       sh.bmin[1][i] = ALL;
       sh.bmax[0][i] = 0u;
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     if (lane == 0) { sh.red_a[wave] = __float_as_uint(xmin); sh.red_b[wave] = __float_as_uint(xmax); }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < TK_WAVES; ++w) {
+    for (int w = 0; w < (THREADS / WAVE); ++w) {
       xmin = fminf(xmin, __uint_as_float(sh.red_a[w]));
       xmax = fmaxf(xmax, __uint_as_float(sh.red_b[w]));
     }
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
         if (v == v) atomicAdd(&sh.hist[0][lin_bin(v, s0, c0)], 1u);
       });
       __syncthreads();
-      select_bin(sh.hist[0], sh.bmin[0], sh.bmax[0], need, sh);
+      select_bin<THREADS>(sh.hist[0], sh.bmin[0], sh.bmax[0], need, sh);
       const uint32_t bin0 = sh.sel_bin;
       need = sh.sel_need;
       if (sh.sel_count <= (uint32_t)WAVE) {
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       float s1 = s0 * (float)TK_BINS;
       float c1 = -(xmin + (float)bin0 / s0) * s1;
       if (!(s1 <= __FLT_MAX__ && c1 <= __FLT_MAX__ && c1 >= -__FLT_MAX__)) { s1 = 0.f; c1 = 0.f; }
-      for (int i = tid; i < TK_HIST; i += TK_THREADS) sh.hist[0][i] = 0;  // read in select_bin
+      for (int i = tid; i < TK_HIST; i += THREADS) sh.hist[0][i] = 0;  // read in select_bin
       visit([&](float v) {
         if (lin_bin(v, s0, c0) == bin0) {
           const uint32_t b = lin_bin(v, s1, c1);
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
         }
       });
       __syncthreads();
-      select_bin(sh.hist[1], sh.bmin[1], sh.bmax[1], need, sh);
+      select_bin<THREADS>(sh.hist[1], sh.bmin[1], sh.bmax[1], need, sh);
       lo = sh.sel_min;
       hi = sh.sel_max;
       count = sh.sel_count;
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       uint32_t* mn = sh.bmin[cur];
       uint32_t* mx = sh.bmax[cur];
       // the other buffers were last read in the previous select_bin; cleared for the next round
-      for (int i = tid; i < TK_BINS; i += TK_THREADS) {
+      for (int i = tid; i < TK_BINS; i += THREADS) {
         sh.hist[cur ^ 1][i] = 0;
         sh.bmin[cur ^ 1][i] = ALL;
         sh.bmax[cur ^ 1][i] = 0u;
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
         }
       });
       __syncthreads();
-      select_bin(hc, mn, mx, need, sh);
+      select_bin<THREADS>(hc, mn, mx, need, sh);
       count = sh.sel_count;
       need = sh.sel_need;
       lo = sh.sel_min;
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     gt_tot = 0;
     eq_tot = 0;
 #pragma unroll
-    for (int w = 0; w < TK_WAVES; ++w) {
+    for (int w = 0; w < (THREADS / WAVE); ++w) {
       const uint32_t a = sh.red_c[w], b = sh.red_d[w];
       if (w < wave) { gt_b += a; eq_b += b; }
       gt_tot += a;
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       __syncthreads();
       uint32_t gt_b = gt_chunk + igt - gt, eq_b = eq_chunk + ieq - eq;
 #pragma unroll
-      for (int w = 0; w < TK_WAVES; ++w) {
+      for (int w = 0; w < (THREADS / WAVE); ++w) {
         const uint32_t a = sh.red_c[w], b = sh.red_d[w];
         if (w < wave) { gt_b += a; eq_b += b; }
         gt_chunk += a;
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
       __syncthreads();
       uint32_t gt_before = gt_chunk, eq_before = eq_chunk;
 #pragma unroll
-      for (int w = 0; w < TK_WAVES; ++w) {
+      for (int w = 0; w < (THREADS / WAVE); ++w) {
         const uint32_t a = sh.red_c[w], b = sh.red_d[w];
         if (w < wave) { gt_before += a; eq_before += b; }
         gt_chunk += a;
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
     else if (take) orow[slot] = pos;
   };
   if (staged)
-    for (int i = tid; i < k; i += TK_THREADS) sh.obuf[i] = -1;
+    for (int i = tid; i < k; i += THREADS) sh.obuf[i] = -1;
 
   float thr = 0.f;
   uint32_t thr_need;
@@ -595,7 +605,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(
   }
   if (staged) {
     __syncthreads();
-    for (int i = tid; i < k; i += TK_THREADS) orow[i] = sh.obuf[i];
+    for (int i = tid; i < k; i += THREADS) orow[i] = sh.obuf[i];
   }
 }
 
@@ -1229,10 +1239,10 @@ hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, 
   return hipGetLastError();
 }
 
-template <int UNITS, int MODE>
+template <int UNITS, int MODE, int THREADS = TK_THREADS>
 hipError_t launch_rows(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                        hipStream_t stream) {
-  topk_rows<UNITS, MODE><<<b.total_q, TK_THREADS, 0, stream>>>(
+  topk_rows<THREADS, UNITS, MODE><<<b.total_q, THREADS, 0, stream>>>(
       scores, ld, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k, k, indices);
   return hipGetLastError();
 }
@@ -1255,6 +1265,9 @@ hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, i
   if (groups <= 2 * TK_THREADS) return launch_rows<2, 0>(b, scores, ld, k, indices, stream);
   if (groups <= 4 * TK_THREADS) return launch_rows<4, 0>(b, scores, ld, k, indices, stream);
   if (groups <= 8 * TK_THREADS) return launch_rows<8, 0>(b, scores, ld, k, indices, stream);
+  // Streamed rows: with enough rows to give every CU two, 512-thread workgroups of half the
+  // chunk let two of them share a CU, so one's barriers and memory waits overlap the other's work.
+  if (k <= TK_OBUF && b.total_q >= 512) return launch_rows<8, 1, 512>(b, scores, ld, k, indices, stream);
   if (k <= TK_OBUF) return launch_rows<8, 1>(b, scores, ld, k, indices, stream);
   return launch_rows<8, 2>(b, scores, ld, k, indices, stream);
 }

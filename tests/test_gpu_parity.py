@@ -628,6 +628,19 @@ def test_topk_many_long_rows():
     _crafted_topk(rows, 2048)
 
 
+def test_topk_streamed_rows_two_workgroups_per_cu():
+    """At least 512 streamed rows (longer than one register chunk, k within the candidate buffer):
+    512-thread workgroups, two per CU, each row in chunks of 16384 positions, with ties and a
+    row shorter than one chunk among them."""
+    rng = np.random.default_rng(12)
+    lens = rng.integers(33000, 41000, 520)
+    rows = [rng.integers(-6, 7, int(n)).astype(np.float32) for n in lens]
+    rows[7] = rng.normal(size=rows[7].shape[0]).astype(np.float32)
+    rows[100] = np.full(int(lens[100]), 2.0, dtype=np.float32)       # one tie group
+    rows[200] = rows[200][:9000]                                       # one chunk
+    _crafted_topk(rows, 2048)
+
+
 def test_topk_many_long_rows_large_k():
     """Rows longer than one register chunk with k above the candidate buffer: every pass
     re-reads the row chunk by chunk."""
