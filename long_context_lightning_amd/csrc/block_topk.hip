@@ -10,7 +10,9 @@
 // topk_blocks * B. The chosen positions come in runs of B consecutive latent rows, which the
 // sparse-MLA gathers read as contiguous memory.
 //
-// Two kernels:
+// Two kernels (one when the longest row has at most 65536 positions: the select then pools its
+// row itself, with the same per-block thread layout and reduction order, so the keys are the
+// same bits):
 //  * pool: a workgroup per (query, 8192 positions): one sequence lookup, then every thread's
 //    eight 16-byte loads of four consecutive scores at once; B/4 adjacent threads per block
 //    combine with lane exchanges and each block's order-preserving 32-bit key goes to the
@@ -105,11 +107,18 @@ constexpr int BT_UNROLL = 4;
 constexpr int BT_STAGE_UNROLL = 8;          // keys per thread and step when staging the row
 constexpr int BT_WPT = BT_MAX_BLOCKS / 32 / BT_THREADS;   // bitmap words per thread (1)
 
-template <int B>
+// POOL = 0: the block keys come from block_pool's workspace; POOL = 1 (max) or 2 (mean): this
+// kernel pools them from the score row itself (rows of at most BT_POOL_MAX positions: one launch
+// instead of two, the row's scores read by one workgroup).
+constexpr int BT_POOL_PASS = 4;             // 16-byte loads per thread and pooling step
+constexpr int BT_POOL_STEP = BT_POOL_PASS * BT_THREADS * 4;   // 16384 positions
+constexpr int64_t BT_POOL_MAX = 4 * BT_POOL_STEP;
+
+template <int B, int POOL>
 __global__ __launch_bounds__(BT_THREADS) void block_select(
-    const uint32_t* __restrict__ keys, int nb_ld, int kb, const int32_t* __restrict__ cu_q,
-    const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k, int64_t ld,
-    int32_t* __restrict__ indices) {
+    const uint32_t* __restrict__ keys, const float* __restrict__ scores, int nb_ld, int kb,
+    const int32_t* __restrict__ cu_q, const int64_t* __restrict__ cu_k, int nseq, int total_q,
+    int64_t total_k, int64_t ld, int32_t* __restrict__ indices) {
   __shared__ uint32_t skey[BT_MAX_BLOCKS];
   __shared__ uint32_t hist[BT_BINS];
   __shared__ uint32_t red[BT_WAVES];
@@ -132,8 +141,55 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
   }
   constexpr int STEP = BT_THREADS * BT_UNROLL;
   // the row's keys into LDS with their smallest and largest key
-  const uint32_t* rk = keys + (int64_t)t * nb_ld;
   uint32_t kmin = 0xffffffffu, kmax = 0;
+  if constexpr (POOL > 0) {
+    // pooled here as block_pool does: in each step thread i holds four consecutive positions per
+    // pass, B/4 adjacent threads (in one wave) per block, combined with lane exchanges
+    constexpr int TPB = B / 4;
+    const float* row = scores + (int64_t)t * ld;
+    const int u = tid & (TPB - 1);
+    for (int64_t p0 = 0; p0 < n; p0 += BT_POOL_STEP) {
+      float v[BT_POOL_PASS][4];
+#pragma unroll
+      for (int i = 0; i < BT_POOL_PASS; ++i) {
+        const int64_t s0 = p0 + ((int64_t)i * BT_THREADS + tid) * 4;
+        if (s0 + 3 < n) {
+          const f32x4 x = *(const f32x4*)(row + s0);
+          v[i][0] = x[0]; v[i][1] = x[1]; v[i][2] = x[2]; v[i][3] = x[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[i][e] = s0 + e < n ? row[s0 + e] : NAN;   // not visible
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < BT_POOL_PASS; ++i) {
+        float acc;
+        if constexpr (POOL == 2) {
+          acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc += v[i][e] == v[i][e] ? v[i][e] : 0.f;
+#pragma unroll
+          for (int o = 1; o < TPB; o <<= 1) acc += __shfl_xor(acc, o, WAVE);
+        } else {
+          acc = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = v[i][e] == v[i][e] ? fmaxf(acc, v[i][e]) : acc;
+#pragma unroll
+          for (int o = 1; o < TPB; o <<= 1) acc = fmaxf(acc, __shfl_xor(acc, o, WAVE));
+        }
+        const int64_t s0 = p0 + ((int64_t)i * BT_THREADS + tid) * 4;  // block start if u == 0
+        const int64_t c = s0 / B;
+        if (u == 0 && c < nb) {
+          if constexpr (POOL == 2) acc = acc / (float)min((int64_t)B, n - c * B);
+          const uint32_t kv = pooled_key(acc);
+          skey[c] = kv;
+          kmin = min(kmin, kv);
+          kmax = max(kmax, kv);
+        }
+      }
+    }
+  } else {
+  const uint32_t* rk = keys + (int64_t)t * nb_ld;
   for (int c0 = 0; c0 < nb; c0 += BT_THREADS * BT_STAGE_UNROLL) {
     uint32_t kv[BT_STAGE_UNROLL];
 #pragma unroll
@@ -150,6 +206,7 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
         kmax = max(kmax, kv[u]);
       }
     }
+  }
   }
   kmin = last_lane(wave_incl_scan(kmin, 0xffffffffu, MinU32()));
   kmax = last_lane(wave_incl_scan(kmax, 0u, MaxU32()));
@@ -291,6 +348,15 @@ hipError_t launch_block(const Batch& b, const float* scores, int64_t ld, bool me
                         int32_t* indices, void* workspace, hipStream_t stream) {
   const int nb_ld = (int)((b.max_k + B - 1) / B);
   uint32_t* keys = (uint32_t*)workspace;
+  if (std::min<int64_t>(b.max_k, ld) <= BT_POOL_MAX) {   // pooled inside the select: one launch
+    if (mean)
+      block_select<B, 2><<<dim3(b.total_q), BT_THREADS, 0, stream>>>(
+          nullptr, scores, nb_ld, kb, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k, ld, indices);
+    else
+      block_select<B, 1><<<dim3(b.total_q), BT_THREADS, 0, stream>>>(
+          nullptr, scores, nb_ld, kb, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k, ld, indices);
+    return hipGetLastError();
+  }
   constexpr int CHUNK = POOL_PASSES * POOL_THREADS * 4;
   const dim3 pgrid((unsigned)(((int64_t)nb_ld * B + CHUNK - 1) / CHUNK), b.total_q);
   if (mean)
@@ -301,9 +367,10 @@ hipError_t launch_block(const Batch& b, const float* scores, int64_t ld, bool me
                                                              b.total_q, b.total_k, nb_ld, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  block_select<B><<<dim3(b.total_q), BT_THREADS, 0, stream>>>(keys, nb_ld, kb, b.cu_q, b.cu_k,
-                                                              b.nseq, b.total_q, b.total_k, ld,
-                                                              indices);
+  block_select<B, 0><<<dim3(b.total_q), BT_THREADS, 0, stream>>>(keys, nullptr, nb_ld, kb,
+                                                                 b.cu_q, b.cu_k, b.nseq,
+                                                                 b.total_q, b.total_k, ld,
+                                                                 indices);
   return hipGetLastError();
 }
 
