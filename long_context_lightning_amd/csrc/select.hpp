@@ -7,13 +7,16 @@
 // Scores enter as order-preserving keys (score_key; -0.0 and +0.0 share a key, and no score
 // gives key 0, which marks an absent position). Thread i holds PER keys of consecutive
 // positions, thread i's before thread i+1's.
-//   rounds: three radix digits of the key (bits 31..21, 20..10, 9..0), each counted in a
-//           2048-bin LDS histogram over the keys that share the digits found so far, give the
-//           threshold key (the k-th largest) and how many keys equal to it are taken. Every wave
-//           finds the bin by itself (lane l sums 32 bins, a wave prefix sum picks the lane, then
-//           each lane takes one of that lane's bins and a second prefix sum picks the bin), so a
-//           round costs one barrier (round 0's histogram is counted by sel_count0 before the
-//           barrier that precedes sel_threshold);
+//   rounds: radix digits of the key (bits 31..21, 20..10, 9..0), each counted in a 2048-bin
+//           LDS histogram over the keys that share the digits found so far, give the threshold
+//           key (the k-th largest) and how many keys equal to it are taken. Every wave finds the
+//           bin by itself (lane l sums 32 bins, a wave prefix sum picks the lane, then each lane
+//           takes one of that lane's bins and a second prefix sum picks the bin), so a round
+//           costs one barrier (round 0's histogram is counted by sel_count0 before the barrier
+//           that precedes sel_threshold). Round 1 also records, per bin, whether its keys share
+//           their low ten bits; when the chosen bin holds a single key value that value is the
+//           threshold and round 2 is skipped (scores that differ in their top 22 key bits, e.g.
+//           integers of magnitude below 2^14, never need it);
 //   ranks:  each thread's taken keys as a bit mask (keys above the threshold, and of the keys
 //           equal to it the first ones in position order, as many as are taken); workgroup
 //           prefix sums of the counts above and equal give each thread the rank of its first
@@ -33,8 +36,9 @@ constexpr int SEL_BINS = 2048;
 constexpr int SEL_PADDED = SEL_BINS + SEL_BINS / 32;
 constexpr int SEL_HIST = SEL_PADDED + WAVE;
 constexpr int SEL_H1 = SEL_HIST;             // round 1's histogram (round 0's at word 0)
-constexpr int SEL_H2 = 2 * SEL_HIST;         // round 2's
-constexpr int SEL_RED = 3 * SEL_HIST;        // [2][waves] prefix-sum partials
+constexpr int SEL_LOW = 2 * SEL_HIST;        // round 1's low-bit summary per bin (see below)
+constexpr int SEL_H2 = 3 * SEL_HIST;         // round 2's
+constexpr int SEL_RED = 4 * SEL_HIST;        // [2][waves] prefix-sum partials
 template <int THREADS>
 constexpr int sel_scratch_words() { return SEL_RED + 2 * (THREADS / WAVE); }
 
@@ -102,8 +106,8 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* __restrict__ hc, ui
   rem = need - min(__builtin_amdgcn_readlane(cum, j), need);
 }
 
-// Zeroes the first `hists` histograms of the scratch (a barrier must follow before they are
-// counted into).
+// Zeroes the first `hists` histograms of the scratch (round 0's, round 1's and the low-bit
+// summaries are the first three; a barrier must follow before they are counted into).
 template <int THREADS>
 __device__ __forceinline__ void sel_clear(uint32_t* __restrict__ scratch, int hists) {
   for (int i = threadIdx.x; i < hists * SEL_HIST; i += THREADS) scratch[i] = 0;
@@ -126,7 +130,11 @@ struct SelThreshold {
 };
 
 // The threshold of the workgroup's keys for k (at least k keys present). Histogram 0 holds round
-// 0's counts and was published by a barrier; histogram 1 is zero. Two barriers.
+// 0's counts and was published by a barrier; histogram 1 and the low-bit summaries are zero. One
+// or two barriers: round 1 also ORs, per fine bin, the low ten bits of each key and their
+// complement into one word, so that when the chosen fine bin holds a single key value (its keys'
+// low bits OR to a value disjoint from their complements' OR) that value is the threshold and
+// round 2 is skipped.
 template <int THREADS, int PER>
 __device__ __forceinline__ SelThreshold sel_threshold(const uint32_t (&key)[PER], uint32_t k,
                                                       uint32_t* __restrict__ scratch) {
@@ -142,11 +150,23 @@ __device__ __forceinline__ SelThreshold sel_threshold(const uint32_t (&key)[PER]
     for (int i = threadIdx.x; i < SEL_HIST; i += THREADS) scratch[SEL_H2 + i] = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if ((key[i] >> 21) == pref) atomicAdd(&hc[sel_slot((key[i] >> 10) & 2047u)], 1u);
+      if ((key[i] >> 21) == pref) {
+        const uint32_t sl = sel_slot((key[i] >> 10) & 2047u);
+        atomicAdd(&hc[sl], 1u);
+        atomicOr(&scratch[SEL_LOW + sl], (key[i] & 1023u) | ((~key[i] & 1023u) << 10));
+      }
     __syncthreads();
     sel_find_bin(hc, need, bin, need);
   }
   pref = (pref << 11) | bin;                   // bits 31..10
+  {
+    const uint32_t lo = scratch[SEL_LOW + sel_slot(bin)];
+    if (((lo & 1023u) & (lo >> 10)) == 0) {   // uniform: one key value in the chosen bin
+      r.thr = (pref << 10) | (lo & 1023u);
+      r.need = need;
+      return r;
+    }
+  }
   // round 2: bits 9..0 (H2; bins 1024.. stay empty)
   {
     uint32_t* hc = scratch + SEL_H2;

@@ -137,16 +137,23 @@ constexpr int SEL_SCRATCH_WORDS = SEL_LIST_AT + SEL_LIST;
 static_assert(SEL_SCRATCH_WORDS * 4 <= STAGE_BYTES, "fused selection scratch must fit one stage");
 
 // Writes idx_row[r] for r in [r_beg, r_end) (r_end - r_beg <= SEL_LIST) from the scores v of
-// positions 0..n-1 (sel_load_scores). scratch: SEL_SCRATCH_WORDS words of LDS whose first two
-// histograms were zeroed before a barrier. Every thread of the workgroup calls it.
+// positions 0..n-1 (sel_load_scores), and the slice's first 2*TILE entries also to head (LDS;
+// entries past the slice are left as they are). scratch: SEL_SCRATCH_WORDS words of LDS whose
+// first two histograms and the low-bit summaries were zeroed before a barrier. Every thread of
+// the workgroup calls it; a barrier must follow before head is read.
 template <int PER>
 __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_t n, int k,
                                                    int r_beg, int r_end, int32_t* idx_row,
-                                                   uint32_t* __restrict__ scratch) {
+                                                   uint32_t* __restrict__ scratch,
+                                                   int32_t* __restrict__ head) {
   const int tid = threadIdx.x;
   uint32_t* list = scratch + SEL_LIST_AT;      // [SEL_LIST] the split's slice
   if (n <= k) {                                // dense: every visible position
-    for (int r = r_beg + tid; r < r_end; r += NTHREADS) idx_row[r] = r < n ? r : -1;
+    for (int r = r_beg + tid; r < r_end; r += NTHREADS) {
+      const int32_t x = r < n ? r : -1;
+      idx_row[r] = x;
+      if (r - r_beg < 2 * TILE) head[r - r_beg] = x;
+    }
     return;
   }
   uint32_t key[PER];
@@ -172,7 +179,10 @@ __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_
     ++rk;
   }
   __syncthreads();
-  for (int j = tid; j < r_end - r_beg; j += NTHREADS) idx_row[r_beg + j] = (int32_t)list[j];
+  for (int j = tid; j < r_end - r_beg; j += NTHREADS) {
+    idx_row[r_beg + j] = (int32_t)list[j];
+    if (j < 2 * TILE) head[j] = (int32_t)list[j];
+  }
 }
 
 // grid: 1-D, 8 * ceil(T/8) * nsplit * ceil(H/64) workgroups. Consecutive workgroups are
@@ -182,8 +192,8 @@ __device__ __forceinline__ void fused_select_slice(const float (&v)[PER], int64_
 // queries of one sequence (several decode tokens, a prefill chunk) meet in one L2 and the rows
 // they select in common are fetched from HBM once.
 // FPER > 0: the split's indices are selected from `scores` in the prologue (fused_select_slice,
-// FPER positions per thread)
-// and written to `indices` (the caller's index row) before the tiles read them back.
+// FPER positions per thread) and written to `indices` (the caller's index row); the first two
+// tiles' indices are taken from LDS, the later ones read back from `indices`.
 template <int FPER>
 __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
   if constexpr (FUSED)                                  // issued before the sequence lookup
     sel_load_scores<FPER>(scores + (int64_t)t * ld_scores,
                             min(ld_scores, (int64_t)FUSED_MAX_POS), (ld_scores & 3) == 0, fs);
-  if constexpr (FUSED) sel_clear<NTHREADS>((uint32_t*)stage0, 2);   // (ordered by the lookup's barrier)
+  if constexpr (FUSED) sel_clear<NTHREADS>((uint32_t*)stage0, 3);   // (ordered by the lookup's barrier)
   QueryPos qp;
   {
     int64_t* qs = (int64_t*)rbuf;
@@ -263,10 +273,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_mla_bf16(
     // this split's slice of the index row, then the first two tiles' indices read back (the
     // barrier's workgroup fence orders the stores before the loads)
     const int64_t n = qp.p >= 0 ? min(min(qp.p + 1, ld_scores), (int64_t)FUSED_MAX_POS) : 0;
-    fused_select_slice<FPER>(fs, n, k, r_beg, r_end, idx_out + (int64_t)t * k, (uint32_t*)stage0);
+    int32_t* head = (int32_t*)rbuf + 64;      // past the lookup's words
+    fused_select_slice<FPER>(fs, n, k, r_beg, r_end, idx_out + (int64_t)t * k, (uint32_t*)stage0,
+                             head);
     __syncthreads();
-    i_even = irow[min(r_beg + lane, k - 1)];
-    i_odd = irow[min(r_beg + TILE + lane, k - 1)];
+    // entries past the slice are masked before use
+    i_even = head[lane];
+    i_odd = head[TILE + lane];
   }
   const int64_t L = qp.len;
   const uint32_t Lu = (uint32_t)min(L, (int64_t)0x7fffffff);

@@ -758,6 +758,45 @@ def test_forward_fused_selection_matches_topk(lens, nq, kw):
     check_rows(case, d, scores, shared, {0: o}, {0: l}, rows)
 
 
+def _order_keys(x):
+    """Order-preserving uint32 keys of fp32 scores (-0.0 as +0.0), as the selection defines them."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    u[u == 0x80000000] = 0
+    neg = (u & 0x80000000) != 0
+    return np.where(neg, ~u, u | 0x80000000).astype(np.uint32)
+
+
+def test_forward_fused_selection_real_valued_scores():
+    """Real-valued indexer weights: the threshold's 22-bit key prefix is then often shared by
+    several distinct scores, so the in-launch selection needs its third radix round (integer
+    scores never do). Indices must equal the oracle's top-k of the same scores on every row, and
+    the outputs those of the separate calls; the test also checks on the CPU that some rows do
+    take the third round."""
+    case = _small_case("fused_real", (16384,) * 24 + (9000, 5000, 13000), (1,) * 27)
+    d = DI.make_inputs(case, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    d["w"] = torch.randn(d["w"].shape, generator=g, device="cuda") * 0.37
+    batch = batch_of(case, d)
+    o, l, shared = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk, case.softmax_scale,
+                               case.d_v, q_idx=d["q_idx"], k_idx=d["k_idx"], w=d["w"])
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    idx = dsa.topk(scores, batch, case.index_topk)
+    o2, l2 = dsa.sparse_mla_fwd(d["q"][0], d["kv"][0], idx, batch, case.softmax_scale, case.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(shared, idx)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    topk_all_rows_from_scores(case, scores, shared)
+    third = 0
+    for t, _, p, _ in DI.query_rows(case):
+        keys = _order_keys(scores[t, :p + 1].cpu().numpy())
+        if p + 1 <= case.index_topk:
+            continue
+        thr = np.sort(keys)[::-1][case.index_topk - 1]
+        third += np.unique(keys[(keys >> 10) == (thr >> 10)]).size > 1
+    say(f"  rows needing the third round: {third} of {case.total_q}")
+    assert third > 0
+
+
 def test_forward_fused_selection_equal_scores():
     """Every score equal (zero weights; signed zeros among them): the fused selection takes the
     lowest positions, like dsa_topk."""
