@@ -339,7 +339,9 @@ __global__ __launch_bounds__(BT_THREADS) void block_select(
   __syncthreads();
   for (int j = tid; j < nout; j += BT_THREADS) {
     const int64_t pos = (int64_t)sel[j / B] * B + (j % B);
-    out[j] = pos < n ? (int32_t)pos : -1;     // only the last chosen block can be partial
+    // only the last chosen block can be partial; non-temporal: read by the next launch, so not
+    // left dirty in L2 at this one's end
+    __builtin_nontemporal_store(pos < n ? (int32_t)pos : -1, out + j);
   }
 }
 

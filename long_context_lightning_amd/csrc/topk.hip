@@ -605,7 +605,8 @@ __global__ __launch_bounds__(THREADS, 4) void topk_rows(
   }
   if (staged) {
     __syncthreads();
-    for (int i = tid; i < k; i += THREADS) orow[i] = sh.obuf[i];
+    // non-temporal: read by the next launch, so not left dirty in L2 at this one's end
+    for (int i = tid; i < k; i += THREADS) __builtin_nontemporal_store(sh.obuf[i], orow + i);
   }
 }
 
