@@ -744,13 +744,31 @@ __device__ __forceinline__ void wg_sum2(uint32_t& a, uint32_t& b, SplitShared& s
   __syncthreads();
 }
 
-// In histogram h (global or LDS; SP_BPT consecutive bins per thread, keys counted from the top
-// bin down), finds the bin holding the need-th largest key and publishes it with the keys
-// still needed from it, its count and, when mn / mx are given, its smallest and largest key.
-// If the histogram holds fewer than `need` keys, sel_count is 0. Three barriers (the first one
-// lets every thread finish reading the previous select's results).
-__device__ __forceinline__ void split_select(const uint32_t* h, const uint32_t* mn,
-                                             const uint32_t* mx, uint32_t need,
+// This thread's slice (SP_BPT consecutive bins) of a histogram and, optionally, of its bins'
+// smallest and largest keys. The split kernels load the slices of the row's global histograms
+// right after the sequence lookup, ahead of their chunk's scores, so that the selects run while
+// the scores are still arriving.
+struct SplitSlice {
+  uint32_t h[SP_BPT], mn[SP_BPT], mx[SP_BPT];
+};
+
+__device__ __forceinline__ void split_slice_load(const uint32_t* h, const uint32_t* mn,
+                                                 const uint32_t* mx, SplitSlice& sl) {
+  const int b = SP_BPT * threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < SP_BPT; ++j) {
+    sl.h[j] = h[b + j];
+    sl.mn[j] = mn ? mn[b + j] : 0u;
+    sl.mx[j] = mx ? mx[b + j] : 0u;
+  }
+}
+
+// In a histogram held as per-thread slices (keys counted from the top bin down), finds the bin
+// holding the need-th largest key and publishes it with the keys still needed from it, its
+// count and its smallest and largest key (as the slices hold them). If the histogram holds
+// fewer than `need` keys, sel_count is 0. Three barriers (the first one lets every thread finish
+// reading the previous select's results).
+__device__ __forceinline__ void split_select(const SplitSlice& sl, uint32_t need,
                                              SplitShared& sh) {
   __syncthreads();
   const int tid = threadIdx.x;
@@ -759,7 +777,7 @@ __device__ __forceinline__ void split_select(const uint32_t* h, const uint32_t* 
   uint32_t s = 0;
 #pragma unroll
   for (int j = 0; j < SP_BPT; ++j) {
-    hv[j] = h[SP_BPT * tid + j];
+    hv[j] = sl.h[j];
     s += hv[j];
   }
   const uint32_t incl = wave_incl_scan_u32(s);
@@ -778,12 +796,21 @@ __device__ __forceinline__ void split_select(const uint32_t* h, const uint32_t* 
       sh.sel_bin = b;
       sh.sel_need = need - above;
       sh.sel_count = hv[j];
-      sh.sel_min = mn ? mn[b] : 0u;
-      sh.sel_max = mx ? mx[b] : 0u;
+      sh.sel_min = sl.mn[j];
+      sh.sel_max = sl.mx[j];
     }
     above += hv[j];
   }
   __syncthreads();
+}
+
+// The same on a histogram in memory (global or LDS; mn / mx may be null).
+__device__ __forceinline__ void split_select(const uint32_t* h, const uint32_t* mn,
+                                             const uint32_t* mx, uint32_t need,
+                                             SplitShared& sh) {
+  SplitSlice sl;
+  split_slice_load(h, mn, mx, sl);
+  split_select(sl, need, sh);
 }
 
 // Bins of the first two rounds of a row, from its smallest and largest score (every workgroup of
@@ -796,9 +823,16 @@ struct SplitBins {
   int shift0;
 };
 
-__device__ __forceinline__ SplitBins split_bins(const float2* mm, int nchunks, SplitShared& sh) {
-  float mn = __int_as_float(0x7f800000), mx = -mn;
-  for (int i = threadIdx.x; i < nchunks; i += SP_THREADS) {
+// The first SP_THREADS chunk extremes of a row, one per thread (loaded ahead of the scores).
+__device__ __forceinline__ float2 split_minmax_load(const float2* mm, int nchunks) {
+  const float inf = __int_as_float(0x7f800000);
+  return (int)threadIdx.x < nchunks ? mm[threadIdx.x] : make_float2(inf, -inf);
+}
+
+__device__ __forceinline__ SplitBins split_bins(const float2* mm, float2 first, int nchunks,
+                                                SplitShared& sh) {
+  float mn = first.x, mx = first.y;
+  for (int i = threadIdx.x + SP_THREADS; i < nchunks; i += SP_THREADS) {
     const float2 v = mm[i];
     mn = fminf(mn, v.x);
     mx = fmaxf(mx, v.y);
@@ -872,7 +906,9 @@ struct SplitChoice {
   uint32_t lo, hi, count, need;
 };
 
-__device__ __forceinline__ SplitChoice split_choice(const SplitBins& sb, const uint32_t* rw, int k,
+// h0, h1: the row's round-0 histogram and its fine histogram with bin extremes, as slices.
+__device__ __forceinline__ SplitChoice split_choice(const SplitBins& sb, const SplitSlice& h0,
+                                                    const SplitSlice& h1, int k,
                                                     SplitShared& sh) {
   SplitChoice ch;
   if (sb.mode == 0) {                            // one value: take the first k of them
@@ -881,9 +917,9 @@ __device__ __forceinline__ SplitChoice split_choice(const SplitBins& sb, const u
     ch.need = (uint32_t)k;
     return ch;
   }
-  split_select(rw + RW_HIST0, nullptr, nullptr, (uint32_t)k, sh);
+  split_select(h0, (uint32_t)k, sh);
   const uint32_t need1 = sh.sel_need;
-  split_select(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, need1, sh);
+  split_select(h1, need1, sh);
   ch.lo = sh.sel_min;
   ch.hi = sh.sel_max;
   ch.count = sh.sel_count;
@@ -920,10 +956,12 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_hist0(
   __shared__ SplitShared sh;
   const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
   if (r.dense || r.c >= r.nchunks) return;
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
   float x[SP_UNITS][4];
   split_load(r, x);
   for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) sh.hist[i] = 0;
-  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
   if (sb.mode == 0) return;
 #pragma unroll
   for (int u = 0; u < SP_UNITS; ++u)
@@ -944,6 +982,11 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_hist1(
   __shared__ SplitShared sh;
   const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
   if (r.dense || r.c >= r.nchunks) return;
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
+  SplitSlice h0;
+  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
   float x[SP_UNITS][4];
   split_load(r, x);
   for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) {
@@ -951,10 +994,9 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_hist1(
     sh.bmin[i] = 0xffffffffu;
     sh.bmax[i] = 0u;
   }
-  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
   if (sb.mode == 0) return;
-  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
-  split_select(rw + RW_HIST0, nullptr, nullptr, (uint32_t)k, sh);
+  split_select(h0, (uint32_t)k, sh);
   const uint32_t bin0 = sh.sel_bin;
   const SplitBins1 b1 = split_bins1(sb, bin0);
 #pragma unroll
@@ -987,11 +1029,16 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_count(
   __shared__ SplitShared sh;
   const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
   if (r.dense || r.c >= r.nchunks) return;
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
+  SplitSlice h0, h1;
+  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
+  split_slice_load(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, h1);
   float x[SP_UNITS][4];
   split_load(r, x);
-  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
-  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
-  const SplitChoice ch = split_choice(sb, rw, k, sh);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
+  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
   const float vlo = key_value(ch.lo), vhi = key_value(ch.hi);
   uint32_t above = 0, inside = 0;
 #pragma unroll
@@ -1080,11 +1127,12 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
     return;
   }
   if (r.c >= r.nchunks) return;
-  float x[SP_UNITS][4];
-  split_load(r, x);
-  const SplitBins sb = split_bins(ws.minmax + (int64_t)r.t * ws.max_chunks, r.nchunks, sh);
   const uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
-  const SplitChoice ch = split_choice(sb, rw, k, sh);
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
+  SplitSlice h0, h1;
+  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
+  split_slice_load(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, h1);
   // counts of the chunks before this one
   uint32_t above_b = 0, inside_b = 0;
   const uint2* cnt = ws.counts + (int64_t)r.t * ws.max_chunks;
@@ -1093,6 +1141,10 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
     above_b += v.x;
     inside_b += v.y;
   }
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
+  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
   wg_sum2(above_b, inside_b, sh);
   float thr;
   uint32_t thr_need, gt_before, eq_before;
