@@ -153,6 +153,12 @@ __global__ __launch_bounds__(THREADS, 4) void topk_rows(
   const int wave = tid >> 6;
   const float* srow = scores + (int64_t)t * ld;
   // The row is read in aligned 16-byte groups; `off` floats of the first group precede it.
+  // For the first row of a score matrix that does not start on a 16-byte boundary, and the
+  // last row of one that does not end on one, an edge group reaches up to 12 bytes outside the
+  // buffer, but only inside the aligned 16 bytes that also hold a buffer element, so never
+  // into another page; the positions outside the row are masked before use. Reading those
+  // groups element by element instead makes the compiler wait for every outstanding load at
+  // each use, which costs the split top-k about 6 us per call.
   // Positions fit in 32 bits (they are stored as int32).
   const int off = (int)((reinterpret_cast<uintptr_t>(srow) >> 2) & 3);
   const f32x4* g4 = reinterpret_cast<const f32x4*>(srow - off);

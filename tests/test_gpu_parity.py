@@ -571,6 +571,40 @@ def _crafted_topk(rows_scores, k):
         assert np.array_equal(got[i], want), (i, len(r), np.sum(got[i] != want))
 
 
+def _crafted_topk_at(rows_scores, k, shift):
+    """As _crafted_topk, with every row of length ld = the longest row, the score matrix starting
+    `shift` floats into its buffer and ending where the buffer ends."""
+    lens = [len(r) for r in rows_scores]
+    batch = dsa.Batch.from_lengths([1] * len(lens), lens)
+    T, ld = len(lens), max(lens)
+    buf = torch.zeros(shift + T * ld, dtype=torch.float32)
+    sc = buf[shift:].view(T, ld)
+    for i, r in enumerate(rows_scores):
+        sc[i, :len(r)] = torch.from_numpy(np.asarray(r, dtype=np.float32))
+    gbuf = buf.cuda()
+    idx = dsa.topk(gbuf[shift:].view(T, ld), batch, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for i, r in enumerate(rows_scores):
+        want = O.topk_row(np.asarray(r, dtype=np.float32).astype(np.float64), k)
+        assert np.array_equal(got[i], want), (i, len(r), np.sum(got[i] != want))
+
+
+@pytest.mark.parametrize("shift", [1, 3])
+def test_topk_unaligned_rows_to_the_buffer_end(shift):
+    """Score rows that start off a 16-byte boundary (odd row length, matrix offset into its
+    buffer) and are visible to their last position: each row's first and last 16-byte groups
+    straddle the row's ends and are read element by element, so no read leaves the buffer. The
+    oracle's top-k on the split-row path (8 rows of 40001), the register path (80 rows of 20001)
+    and the streamed path (70 rows of 70001)."""
+    rng = np.random.default_rng(40 + shift)
+    for T, L in ((8, 40001), (80, 20001), (70, 70001)):
+        rows = [rng.integers(-50, 51, L).astype(np.float32) for _ in range(T)]
+        rows[1] = rng.normal(size=L).astype(np.float32)
+        rows[-1][-3:] = 1000.0                     # the last row's last positions are selected
+        _crafted_topk_at(rows, 2048, shift)
+
+
 def test_topk_crafted_rows():
     rng = np.random.default_rng(5)
     rows = []
