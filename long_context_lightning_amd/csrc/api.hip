@@ -120,6 +120,26 @@ size_t select_bytes(const Batch& b, int32_t k) {
   return align_up(std::max(dsa::topk_workspace_bytes(b, k), dsa::block_topk_workspace_bytes(b, 4)));
 }
 
+// The launches of dsa_indexer_scores / dsa_indexer_scores_fp8 / dsa_topk after their argument
+// checks. The decode indexer kernels also zero-fill `zero` on the side (then *zeroed is true),
+// which lets the one-launch split top-k of the same step skip its own zero-fill launch.
+dsa_status run_indexer(const dsa_batch* batch, const void* q_idx, const void* k_idx,
+                       const float* k_scale, const float* w, int32_t index_n_heads,
+                       int32_t index_head_dim, dsa_dtype dtype, float* scores, int64_t ld,
+                       hipStream_t stream, dsa::ZeroFill zero = {}, bool* zeroed = nullptr) {
+  if (zeroed) *zeroed = false;
+  if (batch->total_q == 0 || batch->total_k == 0) return DSA_OK;
+  const Batch b = to_batch(batch);
+  if (dtype == DSA_FP8_E4M3)
+    return from_hip(dsa::launch_indexer_fp8(b, q_idx, k_idx, k_scale, w, index_n_heads, scores,
+                                            ld, stream, zero, zeroed));
+  if (dtype == DSA_BF16)
+    return from_hip(dsa::launch_indexer_bf16(b, q_idx, k_idx, w, index_n_heads, scores, ld,
+                                             stream, zero, zeroed));
+  return from_hip(dsa::launch_indexer_f32(b, (const float*)q_idx, (const float*)k_idx, w,
+                                          index_n_heads, index_head_dim, scores, ld, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,14 +153,8 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
   dsa_status st = check_indexer(batch, q_idx, k_idx, w, index_n_heads, index_head_dim, dtype,
                                 ld_scores);
   if (st != DSA_OK) return st;
-  if (batch->total_q == 0 || batch->total_k == 0) return DSA_OK;
-  const Batch b = to_batch(batch);
-  if (dtype == DSA_BF16)
-    return from_hip(dsa::launch_indexer_bf16(b, q_idx, k_idx, w, index_n_heads, scores,
-                                             ld_scores, stream));
-  return from_hip(dsa::launch_indexer_f32(b, (const float*)q_idx, (const float*)k_idx, w,
-                                          index_n_heads, index_head_dim, scores, ld_scores,
-                                          stream));
+  return run_indexer(batch, q_idx, k_idx, nullptr, w, index_n_heads, index_head_dim, dtype,
+                     scores, ld_scores, stream);
 }
 
 dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, const void* k_idx,
@@ -151,9 +165,8 @@ dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, con
   dsa_status st = check_indexer(batch, q_idx, k_idx, w, index_n_heads, index_head_dim,
                                 DSA_FP8_E4M3, ld_scores);
   if (st != DSA_OK) return st;
-  if (batch->total_q == 0 || batch->total_k == 0) return DSA_OK;
-  return from_hip(dsa::launch_indexer_fp8(to_batch(batch), q_idx, k_idx, k_scale, w,
-                                          index_n_heads, scores, ld_scores, stream));
+  return run_indexer(batch, q_idx, k_idx, k_scale, w, index_n_heads, index_head_dim,
+                     DSA_FP8_E4M3, scores, ld_scores, stream);
 }
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
@@ -285,14 +298,22 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
   }
   if (batch->total_q == 0) return DSA_OK;
   if (compute_indices) {
-    st = a->index_fp8
-             ? dsa_indexer_scores_fp8(batch, a->q_idx, a->k_idx, a->k_idx_scale, a->w,
-                                      a->index_n_heads, a->index_head_dim, scores, ld, stream)
-             : dsa_indexer_scores(batch, a->q_idx, a->k_idx, a->w, a->index_n_heads,
-                                  a->index_head_dim, a->dtype, scores, ld, stream);
-    if (st != DSA_OK) return st;
     const dsa::MlaPlan fplan = dsa::plan_sparse_mla_bf16(b, a->index_topk, a->n_heads);
-    if (a->block_size == 0 && a->dtype == DSA_BF16 && dsa::fused_select_supported(b, fplan)) {
+    const bool fused =
+        a->block_size == 0 && a->dtype == DSA_BF16 && dsa::fused_select_supported(b, fplan);
+    // the one-launch split top-k needs its row state zero: the decode indexer clears it on the
+    // side, so the top-k needs no zero-fill launch of its own
+    dsa::ZeroFill zero;
+    if (!fused && a->block_size == 0 && ((uintptr_t)(ws + s_bytes) & 15) == 0) {
+      zero.words = dsa::topk_state_words(b, a->index_topk);
+      zero.p = zero.words > 0 ? (uint32_t*)(ws + s_bytes) : nullptr;
+    }
+    bool zeroed = false;
+    st = run_indexer(batch, a->q_idx, a->k_idx, a->index_fp8 ? a->k_idx_scale : nullptr, a->w,
+                     a->index_n_heads, a->index_head_dim, idx_dt, scores, ld, stream, zero,
+                     &zeroed);
+    if (st != DSA_OK) return st;
+    if (fused) {
       // rows of at most 16384 positions: the sparse-MLA kernel selects each query's top-k in its
       // prologue (one launch fewer); it writes shared_indices as dsa_topk would
       return from_hip(dsa::launch_sparse_mla_bf16(b, a->q, a->kv, shared_indices, a->index_topk,
@@ -304,8 +325,8 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* a, int32_
              ? dsa_block_topk(batch, scores, ld, a->block_size, (dsa_pool)a->pool,
                               a->index_topk / a->block_size, shared_indices, ws + s_bytes,
                               t_bytes, stream)
-             : dsa_topk(batch, scores, ld, a->index_topk, shared_indices, ws + s_bytes, t_bytes,
-                        stream);
+             : from_hip(dsa::launch_topk(b, scores, ld, a->index_topk, shared_indices,
+                                         ws + s_bytes, stream, zeroed));
     if (st != DSA_OK) return st;
   }
   return dsa_sparse_mla_fwd(batch, a->q, a->kv, shared_indices, a->index_topk, a->n_heads,

@@ -213,15 +213,39 @@ __device__ __forceinline__ SeqSpan seq_of_row(const int32_t* __restrict__ cu_q,
   return r;
 }
 
-// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK, y = group of NQ query offsets within its
-// sequence (NQ consecutive new tokens share the key stream).
+// Words zero-filled per workgroup of the side job below (16 per thread).
+constexpr int ZF_WORDS = 256 * 16;
+
+// Side job of a decode launch: workgroups past the key range (x >= the key blocks, y == 0)
+// zero-fill `zero` (the state the next launch of the step needs cleared) and leave. Returns
+// true for those workgroups.
+__device__ __forceinline__ bool zero_fill_block(const ZeroFill& zero, int64_t total_k,
+                                                int keys_per_block) {
+  const int64_t kblocks = (total_k + keys_per_block - 1) / keys_per_block;
+  if ((int64_t)blockIdx.x < kblocks) return false;
+  if (blockIdx.y == 0) {
+    const int64_t base = ((int64_t)blockIdx.x - kblocks) * ZF_WORDS + 4 * threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < ZF_WORDS / 1024; ++i) {
+      const int64_t w = base + 1024 * i;
+      if (w + 3 < zero.words) *(u32x4*)(zero.p + w) = u32x4{0u, 0u, 0u, 0u};
+      else
+        for (int64_t j = w; j < zero.words && j < w + 4; ++j) zero.p[j] = 0u;
+    }
+  }
+  return true;
+}
+
+// grid: x = flattened key rows / DEC_KEYS_PER_BLOCK (then the zero-fill workgroups), y = group
+// of NQ query offsets within its sequence (NQ consecutive new tokens share the key stream).
 template <int HB, int NQ>
 __global__ __launch_bounds__(256) void indexer_decode_bf16(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
     const float* __restrict__ w, const int32_t* __restrict__ cu_q,
     const int64_t* __restrict__ cu_k, int nseq, int total_q, int64_t total_k,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, ZeroFill zero) {
   __shared__ bf16x8 xbuf[DEC_WAVES][DEC_STEP * 16];   // one step of key rows per wave
+  if (zero_fill_block(zero, total_k, DEC_KEYS_PER_BLOCK)) return;
   // wave-uniform (a scalar register): the key range and the step loop below are then uniform,
   // so the loop runs on scalar branches and the compiler's memory-counter waits stay exact
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -394,7 +418,8 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const float* __restrict__ w,
     const int32_t* __restrict__ cu_q, const int64_t* __restrict__ cu_k, int nseq, int total_q,
-    int64_t total_k, float* __restrict__ scores, int64_t ld) {
+    int64_t total_k, float* __restrict__ scores, int64_t ld, ZeroFill zero) {
+  if (zero_fill_block(zero, total_k, F8_KEYS_PER_BLOCK)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int j = blockIdx.y;
@@ -695,7 +720,8 @@ __global__ __launch_bounds__(256) void indexer_f32(
 
 hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_idx,
                                const float* w, int index_n_heads, float* scores, int64_t ld,
-                               hipStream_t stream) {
+                               hipStream_t stream, ZeroFill zero, bool* zeroed) {
+  if (zeroed) *zeroed = false;
   const __bf16* q = (const __bf16*)q_idx;
   const __bf16* k = (const __bf16*)k_idx;
   const bool prefill = b.max_q >= PF_QB;
@@ -715,12 +741,14 @@ hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_
     // 32 indexer heads: up to four new tokens of a sequence share one key stream (their
     // operands stay in registers); 64 heads: one token per stream
     const int nq = index_n_heads == 32 ? std::min(b.max_q, 4) : 1;
-    dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK),
+    const int64_t zblocks = zero.p ? (zero.words + ZF_WORDS - 1) / ZF_WORDS : 0;
+    dim3 grid((unsigned)((b.total_k + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK + zblocks),
               (unsigned)((b.max_q + nq - 1) / nq));
     auto go = [&](auto kern) {
       kern<<<grid, 256, 0, stream>>>(q, k, w, b.cu_q, b.cu_k, b.nseq, b.total_q, b.total_k,
-                                     scores, ld);
+                                     scores, ld, zero);
     };
+    if (zeroed) *zeroed = zero.p != nullptr;
     if (index_n_heads == 64) go(indexer_decode_bf16<2, 1>);
     else if (nq == 1) go(indexer_decode_bf16<1, 1>);
     else if (nq == 2) go(indexer_decode_bf16<1, 2>);
@@ -732,17 +760,20 @@ hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_
 
 hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_idx,
                               const float* k_scale, const float* w, int index_n_heads,
-                              float* scores, int64_t ld, hipStream_t stream) {
+                              float* scores, int64_t ld, hipStream_t stream, ZeroFill zero,
+                              bool* zeroed) {
   const uint8_t* q = (const uint8_t*)q_idx;
   const uint8_t* k = (const uint8_t*)k_idx;
   // as the bf16 kernel: up to four new tokens of a sequence share one key stream (32 heads)
   const int nq = index_n_heads == 32 ? std::min(b.max_q, 4) : 1;
-  dim3 grid((unsigned)((b.total_k + F8_KEYS_PER_BLOCK - 1) / F8_KEYS_PER_BLOCK),
+  const int64_t zblocks = zero.p ? (zero.words + ZF_WORDS - 1) / ZF_WORDS : 0;
+  dim3 grid((unsigned)((b.total_k + F8_KEYS_PER_BLOCK - 1) / F8_KEYS_PER_BLOCK + zblocks),
             (unsigned)((b.max_q + nq - 1) / nq));
   auto go = [&](auto kern) {
     kern<<<grid, 256, 0, stream>>>(q, k, k_scale, w, b.cu_q, b.cu_k, b.nseq, b.total_q,
-                                   b.total_k, scores, ld);
+                                   b.total_k, scores, ld, zero);
   };
+  if (zeroed) *zeroed = zero.p != nullptr;
   auto by_nq = [&](auto scaled) {
     constexpr bool S = decltype(scaled)::value;
     if (index_n_heads == 64) go(indexer_decode_fp8<2, S, 1>);

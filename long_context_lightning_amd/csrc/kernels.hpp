@@ -17,22 +17,34 @@ struct Batch {
   const int64_t* cu_k;
 };
 
-// Step 1: lightning indexer. index_head_dim is 128 on the bf16 path.
+// Words a launch zero-fills on the side (the next step's state), or none.
+struct ZeroFill {
+  uint32_t* p = nullptr;
+  int64_t words = 0;
+};
+
+// Step 1: lightning indexer. index_head_dim is 128 on the bf16 path. The decode kernels also
+// zero-fill `zero` (and then return true in *zeroed); the prefill kernel does not.
 hipError_t launch_indexer_bf16(const Batch& b, const void* q_idx, const void* k_idx,
                                const float* w, int index_n_heads, float* scores, int64_t ld,
-                               hipStream_t stream);
+                               hipStream_t stream, ZeroFill zero = {}, bool* zeroed = nullptr);
 // fp8 (e4m3fn) queries and keys; k_scale [total_k] or null.
 hipError_t launch_indexer_fp8(const Batch& b, const void* q_idx, const void* k_idx,
                               const float* k_scale, const float* w, int index_n_heads,
-                              float* scores, int64_t ld, hipStream_t stream);
+                              float* scores, int64_t ld, hipStream_t stream, ZeroFill zero = {},
+                              bool* zeroed = nullptr);
 hipError_t launch_indexer_f32(const Batch& b, const float* q_idx, const float* k_idx,
                               const float* w, int index_n_heads, int index_head_dim,
                               float* scores, int64_t ld, hipStream_t stream);
 
 // Step 2: causal top-k.
 size_t topk_workspace_bytes(const Batch& b, int k);
+// Words at the start of the top-k workspace that must be zero when the top-k starts (the row
+// state of the one-launch split path), or 0. launch_topk zero-fills them with a launch of its
+// own unless state_zeroed says an earlier launch on the stream already has.
+int64_t topk_state_words(const Batch& b, int k);
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
-                       void* workspace, hipStream_t stream);
+                       void* workspace, hipStream_t stream, bool state_zeroed = false);
 
 // Step 2, block-pooled: blocks of `block` positions scored by their max (or mean) score, the kb
 // best blocks' positions written to indices [T, kb * block]; workspace: block keys.

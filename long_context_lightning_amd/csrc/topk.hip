@@ -619,22 +619,31 @@ __global__ __launch_bounds__(THREADS, 4) void topk_rows(
 // ---------------------------------------------------------------------------------------------
 // Rows split over several workgroups. A batch of a few long rows (long-context decode) leaves
 // most compute units idle under one workgroup per row, so each row is cut into chunks of
-// SP_CHUNK positions, one 256-thread workgroup per chunk with the chunk in registers, and the
-// select runs as five launches that meet through per-row counters in the workspace:
+// SP_CHUNK positions, one 256-thread workgroup per chunk with the chunk in registers. The
+// workgroups of a row meet through per-row state in the workspace.
+//
+// One launch (rows of at most 256 chunks, topk_split_fused): the state is zero-filled first (by
+// the decode indexer of the same step, or by a small launch of its own), then the workgroups of
+// a row meet at three row barriers (device-scope counters and release words, bounded polls):
+//   1  round-0 histogram: 2048 bins of the order-preserving key's top 11 bits, added into the
+//      row's histogram with one global atomic per non-empty bin
+//   2  the bin holding the k-th largest score split by the next 11 key bits (counts only)
+//   3  per chunk, the scores above the chosen fine bin and inside it; when the chosen bin is
+//      neither taken whole nor one value, the positions inside it are appended to a per-row
+//      candidate list
+//   4  every workgroup resolves the threshold (from the candidates when needed, in key space),
+//      sums the counts of the chunks before its own and writes its selected positions in
+//      index order.
+// Five launches (longer rows), whose boundaries order everything:
 //   prep     chunk minimum / maximum; clears the row's histograms
 //   hist0    2048 bins linear between the row's smallest and largest score (bins of a
-//            power-of-two key width when that range is not finite), added into the row's
-//            histogram with one global atomic per non-empty bin
+//            power-of-two key width when that range is not finite)
 //   hist1    the bin holding the k-th largest score split into 2048 finer bins, with each
 //            bin's smallest and largest key
-//   count    per chunk, the scores above the chosen fine bin and inside it; when the chosen
-//            bin neither holds one value nor is taken whole, the positions inside it are
-//            appended to a per-row candidate list
-//   compact  every workgroup resolves the threshold (from the candidates when needed, in key
-//            space), sums the counts of the chunks before its own and writes its selected
-//            positions in index order.
-// Every workgroup of a row derives the same bins from the same global values, so the five
-// launches agree on every decision without a grid-wide barrier.
+//   count    as phase 3 above
+//   compact  as phase 4 above.
+// Every workgroup of a row derives the same bins from the same global values, so they agree on
+// every decision.
 // ---------------------------------------------------------------------------------------------
 constexpr int SP_THREADS = 256;
 constexpr int SP_WAVES = SP_THREADS / WAVE;
@@ -649,7 +658,11 @@ constexpr int RW_HIST1 = TK_BINS;
 constexpr int RW_MIN1 = 2 * TK_BINS;
 constexpr int RW_MAX1 = 3 * TK_BINS;
 constexpr int RW_CAND_N = 4 * TK_BINS;
-constexpr int RW_WORDS = 4 * TK_BINS + 64;
+// Row barrier words of the one-launch path, 256 bytes apart: arrivals of the chunks c with
+// c % 8 == g (8 words), arrivals of completed groups, then the round each group may pass (8).
+constexpr int RW_BAR = 4 * TK_BINS + 64;
+constexpr int BAR_STRIDE = 64;
+constexpr int RW_WORDS = RW_BAR + 17 * BAR_STRIDE;
 
 struct SplitWs {
   uint32_t* rows;      // [total_q][RW_WORDS]
@@ -678,6 +691,69 @@ struct SplitChunk {
   const float* srow;
   const f32x4* g4;
 };
+
+// Workspace words that other workgroups of the same launch write (the one-launch path below)
+// are accessed with relaxed device-scope atomics: an atomic load or store at agent scope is
+// served by the device's coherence point, not by a copy in one XCD's L2, so it sees what a
+// workgroup on another XCD wrote once that workgroup's operation has completed. COH = false is
+// an ordinary access (the five-launch path, where a launch boundary orders everything).
+template <bool COH>
+__device__ __forceinline__ uint32_t ws_ld(const uint32_t* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ void ws_st(uint32_t* p, uint32_t v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ uint64_t ws_ld64(const uint64_t* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ void ws_st64(uint64_t* p, uint64_t v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+// Bound on the polls of one row barrier (each a device-scope load plus a short sleep, about a
+// microsecond): every wave leaves the barrier after at most about a second even if a workgroup
+// of the row never arrived, so the launch always drains (the row's result is then wrong).
+constexpr uint32_t SP_SPIN_LIMIT = 1u << 20;
+
+// Barrier of the workgroups of one row inside one launch, round `round` (1, 2, ..): each wave
+// waits until its own global stores and atomics have completed and the workgroup meets; then
+// one thread counts the workgroup in. Chunks are counted in eight groups (c % 8), so no single
+// word takes every arrival and every poll of a long row: the last arrival of a group counts the
+// group in, the last group sets every group's release word, and each workgroup polls only its
+// group's. Deadlock-free when every row's workgroups can be resident at once: workgroups are
+// dispatched in order, so the lowest unfinished row always has all its workgroups resident and
+// finishes.
+__device__ __forceinline__ void row_barrier(uint32_t* barw, int c, uint32_t n, uint32_t round) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t g = (uint32_t)c & 7u;
+    const uint32_t groups = min(n, 8u);
+    const uint32_t in_group = (n + 7u - g) >> 3;
+    uint32_t* release = barw + (9 + g) * BAR_STRIDE;
+    if (__hip_atomic_fetch_add(barw + g * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) + 1u == round * in_group &&
+        __hip_atomic_fetch_add(barw + 8 * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) + 1u == round * groups) {
+      for (uint32_t j = 0; j < groups; ++j)
+        __hip_atomic_store(barw + (9 + j) * BAR_STRIDE, round, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (uint32_t spin = 0; spin < SP_SPIN_LIMIT; ++spin) {
+      if (__hip_atomic_load(release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= round) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
 
 __device__ __forceinline__ SplitChunk split_chunk(const float* scores, int64_t ld,
                                                   const int32_t* cu_q, const int64_t* cu_k,
@@ -758,14 +834,28 @@ struct SplitSlice {
   uint32_t h[SP_BPT], mn[SP_BPT], mx[SP_BPT];
 };
 
+template <bool COH = false>
 __device__ __forceinline__ void split_slice_load(const uint32_t* h, const uint32_t* mn,
                                                  const uint32_t* mx, SplitSlice& sl) {
   const int b = SP_BPT * threadIdx.x;
 #pragma unroll
   for (int j = 0; j < SP_BPT; ++j) {
-    sl.h[j] = h[b + j];
-    sl.mn[j] = mn ? mn[b + j] : 0u;
-    sl.mx[j] = mx ? mx[b + j] : 0u;
+    sl.h[j] = ws_ld<COH>(h + b + j);
+    sl.mn[j] = mn ? ws_ld<COH>(mn + b + j) : 0u;
+    sl.mx[j] = mx ? ws_ld<COH>(mx + b + j) : 0u;
+  }
+}
+
+// The row's fine histogram with its bins' extremes, as slices. The workspace holds each bin's
+// smallest key complemented (kept with atomicMax), so a cleared row state is all zero.
+template <bool COH = false>
+__device__ __forceinline__ void split_fine_load(const uint32_t* rw, SplitSlice& sl) {
+  const int b = SP_BPT * threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < SP_BPT; ++j) {
+    sl.h[j] = ws_ld<COH>(rw + RW_HIST1 + b + j);
+    sl.mn[j] = ~ws_ld<COH>(rw + RW_MIN1 + b + j);
+    sl.mx[j] = ws_ld<COH>(rw + RW_MAX1 + b + j);
   }
 }
 
@@ -830,9 +920,12 @@ struct SplitBins {
 };
 
 // The first SP_THREADS chunk extremes of a row, one per thread (loaded ahead of the scores).
+template <bool COH = false>
 __device__ __forceinline__ float2 split_minmax_load(const float2* mm, int nchunks) {
   const float inf = __int_as_float(0x7f800000);
-  return (int)threadIdx.x < nchunks ? mm[threadIdx.x] : make_float2(inf, -inf);
+  if ((int)threadIdx.x >= nchunks) return make_float2(inf, -inf);
+  const uint64_t v = ws_ld64<COH>((const uint64_t*)mm + threadIdx.x);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
 __device__ __forceinline__ SplitBins split_bins(const float2* mm, float2 first, int nchunks,
@@ -943,7 +1036,7 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_prep(
   split_load(r, x);
   uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
   for (int i = r.c * SP_THREADS + threadIdx.x; i < RW_WORDS; i += r.nchunks * SP_THREADS)
-    rw[i] = (i >= RW_MIN1 && i < RW_MAX1) ? 0xffffffffu : 0u;
+    rw[i] = 0u;
   float mn = __int_as_float(0x7f800000), mx = -mn;
 #pragma unroll
   for (int u = 0; u < SP_UNITS; ++u)
@@ -1023,28 +1116,20 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_hist1(
     const uint32_t h = sh.hist[i];
     if (h) {
       atomicAdd(&rw[RW_HIST1 + i], h);
-      atomicMin(&rw[RW_MIN1 + i], sh.bmin[i]);
+      atomicMax(&rw[RW_MIN1 + i], ~sh.bmin[i]);
       atomicMax(&rw[RW_MAX1 + i], sh.bmax[i]);
     }
   }
 }
 
-__global__ __launch_bounds__(SP_THREADS) void topk_split_count(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
-    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
-  __shared__ SplitShared sh;
-  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
-  if (r.dense || r.c >= r.nchunks) return;
-  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
-  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
-  const float2 mm0 = split_minmax_load(mm, r.nchunks);
-  SplitSlice h0, h1;
-  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
-  split_slice_load(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, h1);
-  float x[SP_UNITS][4];
-  split_load(r, x);
-  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
-  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
+// The scores above the chosen fine bin and inside it, per chunk (published in ws.counts); when
+// the chosen bin is neither taken whole nor one value, this chunk's positions inside it are
+// appended to the row's candidate list.
+template <bool COH>
+__device__ __forceinline__ void split_count_body(const SplitChunk& r,
+                                                 const float (&x)[SP_UNITS][4],
+                                                 const SplitChoice& ch, const SplitWs& ws,
+                                                 uint32_t* rw, SplitShared& sh) {
   const float vlo = key_value(ch.lo), vhi = key_value(ch.hi);
   uint32_t above = 0, inside = 0;
 #pragma unroll
@@ -1057,7 +1142,9 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_count(
     }
   const uint32_t mine = inside;
   wg_sum2(above, inside, sh);
-  if (threadIdx.x == 0) ws.counts[(int64_t)r.t * ws.max_chunks + r.c] = make_uint2(above, inside);
+  if (threadIdx.x == 0)
+    ws_st64<COH>((uint64_t*)(ws.counts + (int64_t)r.t * ws.max_chunks + r.c),
+                 (uint64_t)above | ((uint64_t)inside << 32));
   if (ch.count == ch.need || ch.lo == ch.hi || inside == 0) return;
   // unresolved: append this chunk's positions inside [lo, hi] to the row's candidate list
   const int wave = threadIdx.x >> 6;
@@ -1075,15 +1162,35 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_count(
     for (int e = 0; e < 4; ++e) {
       const float v = x[u][e];
       if (v >= vlo && v <= vhi) {
-        if (slot < ws.cand_cap) cand[slot] = (uint32_t)(4 * (g0 + u * WAVE) + e - r.off);
+        if (slot < ws.cand_cap) ws_st<COH>(cand + slot, (uint32_t)(4 * (g0 + u * WAVE) + e - r.off));
         ++slot;
       }
     }
 }
 
+__global__ __launch_bounds__(SP_THREADS) void topk_split_count(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  if (r.dense || r.c >= r.nchunks) return;
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
+  SplitSlice h0, h1;
+  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
+  split_fine_load(rw, h1);
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
+  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
+  split_count_body<false>(r, x, ch, ws, rw, sh);
+}
+
 // Threshold among the candidates (keys [lo, hi], `count` of them, `need` to take), in rounds of
 // 2048 key bins of a power-of-two width: the score T and how many scores equal to T are taken
 // (all of them when thr_need is 0xffffffff).
+template <bool COH>
 __device__ __forceinline__ void split_resolve_candidates(const float* srow, const uint32_t* cand,
                                                          uint32_t ncand, SplitChoice ch,
                                                          float& thr, uint32_t& thr_need,
@@ -1102,7 +1209,7 @@ __device__ __forceinline__ void split_resolve_candidates(const float* srow, cons
     }
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
-      const uint32_t kk = score_key(srow[cand[i]]);
+      const uint32_t kk = score_key(srow[ws_ld<COH>(cand + i)]);
       if (kk >= lo && kk <= hi) {
         const uint32_t b = (kk - lo) >> shift;
         atomicAdd(&sh.hist[b], 1u);
@@ -1120,37 +1227,15 @@ __device__ __forceinline__ void split_resolve_candidates(const float* srow, cons
   }
 }
 
-__global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
-    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws,
-    int32_t* __restrict__ out) {
-  __shared__ SplitShared sh;
-  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
-  int32_t* orow = out + (int64_t)r.t * k;
-  if (r.dense) {
-    if (r.c == 0)
-      for (int i = threadIdx.x; i < k; i += SP_THREADS) orow[i] = i < r.ni ? i : -1;
-    return;
-  }
-  if (r.c >= r.nchunks) return;
-  const uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
-  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
-  const float2 mm0 = split_minmax_load(mm, r.nchunks);
-  SplitSlice h0, h1;
-  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
-  split_slice_load(rw + RW_HIST1, rw + RW_MIN1, rw + RW_MAX1, h1);
-  // counts of the chunks before this one
-  uint32_t above_b = 0, inside_b = 0;
-  const uint2* cnt = ws.counts + (int64_t)r.t * ws.max_chunks;
-  for (int i = threadIdx.x; i < r.c; i += SP_THREADS) {
-    const uint2 v = cnt[i];
-    above_b += v.x;
-    inside_b += v.y;
-  }
-  float x[SP_UNITS][4];
-  split_load(r, x);
-  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
-  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
+// Resolves the threshold and writes this chunk's selected positions in index order. above_b /
+// inside_b: this thread's share of the counts of the chunks before this one.
+template <bool COH>
+__device__ __forceinline__ void split_compact_body(const SplitChunk& r,
+                                                   const float (&x)[SP_UNITS][4],
+                                                   const SplitChoice& ch, uint32_t above_b,
+                                                   uint32_t inside_b, const SplitWs& ws,
+                                                   const uint32_t* rw, int k, int32_t* orow,
+                                                   SplitShared& sh) {
   wg_sum2(above_b, inside_b, sh);
   float thr;
   uint32_t thr_need, gt_before, eq_before;
@@ -1166,12 +1251,12 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
     eq_before = inside_b;
   } else {
     const uint32_t* cand = ws.cand + (int64_t)r.t * ws.cand_cap;
-    const uint32_t ncand = (uint32_t)min((int64_t)rw[RW_CAND_N], ws.cand_cap);
-    split_resolve_candidates(r.srow, cand, ncand, ch, thr, thr_need, sh);
+    const uint32_t ncand = (uint32_t)min((int64_t)ws_ld<COH>(rw + RW_CAND_N), ws.cand_cap);
+    split_resolve_candidates<COH>(r.srow, cand, ncand, ch, thr, thr_need, sh);
     const int first_pos = 4 * r.c * SP_CHUNK4 - r.off;
     uint32_t gt = 0, eq = 0;
     for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
-      const uint32_t pos = cand[i];
+      const uint32_t pos = ws_ld<COH>(cand + i);
       if ((int)pos < first_pos) {
         const float v = r.srow[pos];
         gt += v > thr;
@@ -1182,7 +1267,6 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
     gt_before = above_b + gt;
     eq_before = eq;
   }
-
   // compaction of this chunk in index order
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   uint32_t gt = 0, eq = 0;
@@ -1243,6 +1327,143 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
   }
 }
 
+__global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws,
+    int32_t* __restrict__ out) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  int32_t* orow = out + (int64_t)r.t * k;
+  if (r.dense) {
+    if (r.c == 0)
+      for (int i = threadIdx.x; i < k; i += SP_THREADS) orow[i] = i < r.ni ? i : -1;
+    return;
+  }
+  if (r.c >= r.nchunks) return;
+  const uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  const float2* mm = ws.minmax + (int64_t)r.t * ws.max_chunks;
+  const float2 mm0 = split_minmax_load(mm, r.nchunks);
+  SplitSlice h0, h1;
+  split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
+  split_fine_load(rw, h1);
+  // counts of the chunks before this one
+  uint32_t above_b = 0, inside_b = 0;
+  const uint2* cnt = ws.counts + (int64_t)r.t * ws.max_chunks;
+  for (int i = threadIdx.x; i < r.c; i += SP_THREADS) {
+    const uint2 v = cnt[i];
+    above_b += v.x;
+    inside_b += v.y;
+  }
+  float x[SP_UNITS][4];
+  split_load(r, x);
+  const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
+  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
+  split_compact_body<false>(r, x, ch, above_b, inside_b, ws, rw, k, orow, sh);
+}
+
+// Zero-fills the row state of the one-launch path (when no earlier launch of the step did).
+__global__ __launch_bounds__(256) void topk_split_clear(uint32_t* __restrict__ rows, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < words) rows[i] = 0u;
+}
+
+// The split path in one launch: the workgroups of a row meet at three row barriers instead of
+// launch boundaries, and each loads its chunk once. Round 0 bins the order-preserving key's top
+// bits instead of the range between the row's extremes, which saves the extremes' pass. Every value another
+// workgroup of the row produced is read through device-scope atomics (ws_ld), and every value
+// this one publishes is written the same way or with global atomics. Requires the row state
+// zero-filled (topk_split_clear, or an earlier launch of the step) and at most SP_THREADS chunks
+// per row.
+__global__ __launch_bounds__(SP_THREADS) void topk_split_fused(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q,
+    const int64_t* __restrict__ cu_k, int nseq, int64_t total_k, int k, SplitWs ws,
+    int32_t* __restrict__ out) {
+  __shared__ SplitShared sh;
+  const SplitChunk r = split_chunk(scores, ld, cu_q, cu_k, nseq, total_k, k, ws.max_k, ws.max_chunks);
+  int32_t* orow = out + (int64_t)r.t * k;
+  if (r.dense) {
+    if (r.c == 0)
+      for (int i = threadIdx.x; i < k; i += SP_THREADS) orow[i] = i < r.ni ? i : -1;
+    return;
+  }
+  if (r.c >= r.nchunks) return;
+  uint32_t* rw = ws.rows + (int64_t)r.t * RW_WORDS;
+  uint32_t* bar = rw + RW_BAR;
+  const uint32_t n = (uint32_t)r.nchunks;
+  float x[SP_UNITS][4];
+  split_load(r, x);
+
+  // 1. round-0 histogram of the row: 2048 bins of the order-preserving key's top 11 bits
+  // (no pass over the row's extremes first; the fine round splits the chosen bin by the next 11)
+  SplitBins sb;
+  sb.mode = 2;
+  sb.xmin = sb.xmax = 0.f;
+  sb.s0 = sb.c0 = 0.f;
+  sb.lo0 = 0;
+  sb.shift0 = 21;
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) sh.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b = split_bin0(sb, x[u][e]);
+      if (b < (uint32_t)TK_BINS) atomicAdd(&sh.hist[b], 1u);
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS)
+    if (sh.hist[i]) atomicAdd(&rw[RW_HIST0 + i], sh.hist[i]);
+  row_barrier(bar, r.c, n, 1);
+
+  // 2. the bin holding the k-th largest score, split into 2048 fine bins of 2^10 keys (counts
+  // only: a fine bin's key range is known, and an unresolved one goes through the candidates)
+  SplitSlice h0;
+  split_slice_load<true>(rw + RW_HIST0, nullptr, nullptr, h0);
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS) sh.hist[i] = 0;
+  split_select(h0, (uint32_t)k, sh);            // (its first barrier orders the clear)
+  const uint32_t bin0 = sh.sel_bin;
+  const SplitBins1 b1 = split_bins1(sb, bin0);
+#pragma unroll
+  for (int u = 0; u < SP_UNITS; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = x[u][e];
+      if (split_bin0(sb, v) == bin0) atomicAdd(&sh.hist[split_bin1(sb, b1, v)], 1u);
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TK_BINS; i += SP_THREADS)
+    if (sh.hist[i]) atomicAdd(&rw[RW_HIST1 + i], sh.hist[i]);
+  row_barrier(bar, r.c, n, 2);
+
+  // 3. counts above and inside the chosen fine bin; candidates when it is unresolved
+  SplitSlice h1;
+  {
+    const int bb = SP_BPT * threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < SP_BPT; ++j) {
+      // the bin's keys, clamped to those of finite or infinite scores (the keys outside
+      // [key(-inf), key(+inf)] are NaN patterns, which would fail every range comparison)
+      const uint32_t lo = b1.base1 + ((uint32_t)(bb + j) << b1.shift1);
+      h1.h[j] = ws_ld<true>(rw + RW_HIST1 + bb + j);
+      h1.mn[j] = max(lo, 0x007fffffu);
+      h1.mx[j] = min(lo + ((1u << b1.shift1) - 1u), 0xff800000u);
+    }
+  }
+  const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
+  split_count_body<true>(r, x, ch, ws, rw, sh);
+  row_barrier(bar, r.c, n, 3);
+
+  // 4. compaction
+  uint32_t above_b = 0, inside_b = 0;
+  const uint64_t* cnt = (const uint64_t*)(ws.counts + (int64_t)r.t * ws.max_chunks);
+  for (int i = threadIdx.x; i < r.c; i += SP_THREADS) {
+    const uint64_t v = ws_ld64<true>(cnt + i);
+    above_b += (uint32_t)v;
+    inside_b += (uint32_t)(v >> 32);
+  }
+  split_compact_body<true>(r, x, ch, above_b, inside_b, ws, rw, k, orow, sh);
+}
+
 // Layout of the split workspace for this batch; rows.. cand are null when ws is null.
 struct SplitLayout {
   int max_chunks;
@@ -1273,7 +1494,7 @@ bool use_split(const Batch& b, int k) {
 }
 
 hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
-                        void* workspace, hipStream_t stream) {
+                        void* workspace, bool state_zeroed, hipStream_t stream) {
   const SplitLayout L = split_layout(b);
   char* base = (char*)workspace;
   SplitWs ws;
@@ -1285,6 +1506,16 @@ hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, 
   ws.max_k = b.max_k;
   ws.cand_cap = L.cand_cap;
   const unsigned grid = (unsigned)((int64_t)b.total_q * L.max_chunks);
+  if (L.max_chunks <= SP_THREADS) {
+    // one launch once the row state is zero: at most 64 rows of at most 256 chunks are 16384
+    // workgroups of 256 threads, of which one row's (at most 256) are always resident
+    const int64_t words = (int64_t)b.total_q * RW_WORDS;
+    if (!state_zeroed)
+      topk_split_clear<<<(unsigned)((words + 255) / 256), 256, 0, stream>>>(ws.rows, words);
+    topk_split_fused<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
+                                                      b.total_k, k, ws, indices);
+    return hipGetLastError();
+  }
   topk_split_prep<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq, b.total_k,
                                                    k, ws);
   topk_split_hist0<<<grid, SP_THREADS, 0, stream>>>(scores, ld, b.cu_q, b.cu_k, b.nseq,
@@ -1312,9 +1543,16 @@ size_t topk_workspace_bytes(const Batch& b, int k) {
   return use_split(b, k) ? split_layout(b).bytes : 0;
 }
 
+int64_t topk_state_words(const Batch& b, int k) {
+  if (!use_split(b, k)) return 0;
+  const SplitLayout L = split_layout(b);
+  return L.max_chunks <= SP_THREADS ? (int64_t)b.total_q * RW_WORDS : 0;
+}
+
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
-                       void* workspace, hipStream_t stream) {
-  if (use_split(b, k)) return launch_split(b, scores, ld, k, indices, workspace, stream);
+                       void* workspace, hipStream_t stream, bool state_zeroed) {
+  if (use_split(b, k))
+    return launch_split(b, scores, ld, k, indices, workspace, state_zeroed, stream);
   // Registers per thread sized for the longest visible row (16-byte groups, plus one when rows
   // do not all start on a 16-byte boundary); rows longer than 32K keys are processed in chunks.
   const int64_t longest = std::min<int64_t>(b.max_k, ld);

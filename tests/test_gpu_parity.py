@@ -695,6 +695,18 @@ def test_topk_split_rows_mixed_lengths():
     _crafted_topk(rows, 6000)
 
 
+def test_topk_split_rows_beyond_one_launch():
+    """Rows of more than 256 chunks of 8192 positions take the five-launch split path (the
+    one-launch path, whose row barriers need every chunk of a row resident, takes every shorter
+    row): a row of 2,200,001 positions in 41 tie groups, one of 2,097,153 normal scores just past
+    the bound, and a short row beside them."""
+    rng = np.random.default_rng(13)
+    rows = [rng.integers(-20, 21, 2_200_001).astype(np.float32),
+            rng.normal(size=2_097_153).astype(np.float32),
+            rng.normal(size=50000).astype(np.float32)]
+    _crafted_topk(rows, 2048)
+
+
 def test_reference_max_restart_path():
     """Rows whose logits exceed the first tile's maximum by far more than the softmax headroom
     force the attention kernel to raise its reference maxima and redo the split; the result must
