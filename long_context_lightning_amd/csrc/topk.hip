@@ -669,6 +669,7 @@ struct SplitWs {
   float2* minmax;      // [total_q][max_chunks]  chunk min / max score
   uint2* counts;       // [total_q][max_chunks]  chunk (above, inside) the chosen fine bin
   uint32_t* cand;      // [total_q][cand_cap]    positions inside the chosen fine bin
+  uint32_t* candk;     // [total_q][cand_cap]    their keys
   int max_chunks;
   int max_k;
   int64_t cand_cap;
@@ -1162,7 +1163,10 @@ __device__ __forceinline__ void split_count_body(const SplitChunk& r,
     for (int e = 0; e < 4; ++e) {
       const float v = x[u][e];
       if (v >= vlo && v <= vhi) {
-        if (slot < ws.cand_cap) ws_st<COH>(cand + slot, (uint32_t)(4 * (g0 + u * WAVE) + e - r.off));
+        if (slot < ws.cand_cap) {
+          ws_st<COH>(cand + slot, (uint32_t)(4 * (g0 + u * WAVE) + e - r.off));
+          ws_st<COH>(ws.candk + (int64_t)r.t * ws.cand_cap + slot, score_key(v));
+        }
         ++slot;
       }
     }
@@ -1187,14 +1191,37 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_count(
   split_count_body<false>(r, x, ch, ws, rw, sh);
 }
 
+// The row's candidate list as the compaction reads it: its length and the first SP_CREG *
+// SP_THREADS entries (position and key) in registers, loaded in one round with the chunk counts
+// (slots past the list hold stale values and are not used).
+constexpr int SP_CREG = 4;
+struct SplitCands {
+  uint32_t n;
+  uint32_t pos[SP_CREG], key[SP_CREG];
+};
+
+template <bool COH>
+__device__ __forceinline__ void split_cands_load(const SplitWs& ws, const uint32_t* rw, int t,
+                                                 SplitCands& cd) {
+  const uint32_t* cand = ws.cand + (int64_t)t * ws.cand_cap;
+  const uint32_t* candk = ws.candk + (int64_t)t * ws.cand_cap;
+  cd.n = (uint32_t)min((int64_t)ws_ld<COH>(rw + RW_CAND_N), ws.cand_cap);
+#pragma unroll
+  for (int j = 0; j < SP_CREG; ++j) {
+    const int64_t i = min((int64_t)(threadIdx.x + j * SP_THREADS), ws.cand_cap - 1);
+    cd.pos[j] = ws_ld<COH>(cand + i);
+    cd.key[j] = ws_ld<COH>(candk + i);
+  }
+}
+
 // Threshold among the candidates (keys [lo, hi], `count` of them, `need` to take), in rounds of
 // 2048 key bins of a power-of-two width: the score T and how many scores equal to T are taken
 // (all of them when thr_need is 0xffffffff).
 template <bool COH>
-__device__ __forceinline__ void split_resolve_candidates(const float* srow, const uint32_t* cand,
-                                                         uint32_t ncand, SplitChoice ch,
-                                                         float& thr, uint32_t& thr_need,
-                                                         SplitShared& sh) {
+__device__ __forceinline__ void split_resolve_candidates(const SplitCands& cd,
+                                                         const uint32_t* candk,
+                                                         SplitChoice ch, float& thr,
+                                                         uint32_t& thr_need, SplitShared& sh) {
   uint32_t lo = ch.lo, hi = ch.hi, count = ch.count, need = ch.need;
   for (;;) {
     if (count == need) { thr = key_value(lo); thr_need = 0xffffffffu; return; }
@@ -1208,15 +1235,19 @@ __device__ __forceinline__ void split_resolve_candidates(const float* srow, cons
       sh.bmax[i] = 0u;
     }
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
-      const uint32_t kk = score_key(srow[ws_ld<COH>(cand + i)]);
+    auto add = [&](uint32_t kk) {
       if (kk >= lo && kk <= hi) {
         const uint32_t b = (kk - lo) >> shift;
         atomicAdd(&sh.hist[b], 1u);
         atomicMin(&sh.bmin[b], kk);
         atomicMax(&sh.bmax[b], kk);
       }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < SP_CREG; ++j)
+      if (threadIdx.x + j * SP_THREADS < cd.n) add(cd.key[j]);
+    for (uint32_t i = threadIdx.x + SP_CREG * SP_THREADS; i < cd.n; i += SP_THREADS)
+      add(ws_ld<COH>(candk + i));
     __syncthreads();
     split_select(sh.hist, sh.bmin, sh.bmax, need, sh);
     count = sh.sel_count;
@@ -1233,8 +1264,8 @@ template <bool COH>
 __device__ __forceinline__ void split_compact_body(const SplitChunk& r,
                                                    const float (&x)[SP_UNITS][4],
                                                    const SplitChoice& ch, uint32_t above_b,
-                                                   uint32_t inside_b, const SplitWs& ws,
-                                                   const uint32_t* rw, int k, int32_t* orow,
+                                                   uint32_t inside_b, const SplitCands& cd,
+                                                   const SplitWs& ws, int k, int32_t* orow,
                                                    SplitShared& sh) {
   wg_sum2(above_b, inside_b, sh);
   float thr;
@@ -1251,18 +1282,23 @@ __device__ __forceinline__ void split_compact_body(const SplitChunk& r,
     eq_before = inside_b;
   } else {
     const uint32_t* cand = ws.cand + (int64_t)r.t * ws.cand_cap;
-    const uint32_t ncand = (uint32_t)min((int64_t)ws_ld<COH>(rw + RW_CAND_N), ws.cand_cap);
-    split_resolve_candidates<COH>(r.srow, cand, ncand, ch, thr, thr_need, sh);
+    const uint32_t* candk = ws.candk + (int64_t)r.t * ws.cand_cap;
+    split_resolve_candidates<COH>(cd, candk, ch, thr, thr_need, sh);
+    // candidates of the chunks before this one above / equal to the threshold (in key space)
     const int first_pos = 4 * r.c * SP_CHUNK4 - r.off;
+    const uint32_t tk = score_key(thr);
     uint32_t gt = 0, eq = 0;
-    for (uint32_t i = threadIdx.x; i < ncand; i += SP_THREADS) {
-      const uint32_t pos = ws_ld<COH>(cand + i);
+    auto tally = [&](uint32_t pos, uint32_t kk) {
       if ((int)pos < first_pos) {
-        const float v = r.srow[pos];
-        gt += v > thr;
-        eq += v == thr;
+        gt += kk > tk;
+        eq += kk == tk;
       }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < SP_CREG; ++j)
+      if (threadIdx.x + j * SP_THREADS < cd.n) tally(cd.pos[j], cd.key[j]);
+    for (uint32_t i = threadIdx.x + SP_CREG * SP_THREADS; i < cd.n; i += SP_THREADS)
+      tally(ws_ld<COH>(cand + i), ws_ld<COH>(candk + i));
     wg_sum2(gt, eq, sh);
     gt_before = above_b + gt;
     eq_before = eq;
@@ -1346,6 +1382,8 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
   SplitSlice h0, h1;
   split_slice_load(rw + RW_HIST0, nullptr, nullptr, h0);
   split_fine_load(rw, h1);
+  SplitCands cd;
+  split_cands_load<false>(ws, rw, r.t, cd);
   // counts of the chunks before this one
   uint32_t above_b = 0, inside_b = 0;
   const uint2* cnt = ws.counts + (int64_t)r.t * ws.max_chunks;
@@ -1358,7 +1396,7 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_compact(
   split_load(r, x);
   const SplitBins sb = split_bins(mm, mm0, r.nchunks, sh);
   const SplitChoice ch = split_choice(sb, h0, h1, k, sh);
-  split_compact_body<false>(r, x, ch, above_b, inside_b, ws, rw, k, orow, sh);
+  split_compact_body<false>(r, x, ch, above_b, inside_b, cd, ws, k, orow, sh);
 }
 
 // Zero-fills the row state of the one-launch path (when no earlier launch of the step did).
@@ -1453,7 +1491,9 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_fused(
   split_count_body<true>(r, x, ch, ws, rw, sh);
   row_barrier(bar, r.c, n, 3);
 
-  // 4. compaction
+  // 4. compaction: the earlier chunks' counts and the candidate list in one round of loads
+  SplitCands cd;
+  split_cands_load<true>(ws, rw, r.t, cd);
   uint32_t above_b = 0, inside_b = 0;
   const uint64_t* cnt = (const uint64_t*)(ws.counts + (int64_t)r.t * ws.max_chunks);
   for (int i = threadIdx.x; i < r.c; i += SP_THREADS) {
@@ -1461,14 +1501,14 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_fused(
     above_b += (uint32_t)v;
     inside_b += (uint32_t)(v >> 32);
   }
-  split_compact_body<true>(r, x, ch, above_b, inside_b, ws, rw, k, orow, sh);
+  split_compact_body<true>(r, x, ch, above_b, inside_b, cd, ws, k, orow, sh);
 }
 
 // Layout of the split workspace for this batch; rows.. cand are null when ws is null.
 struct SplitLayout {
   int max_chunks;
   int64_t cand_cap;
-  size_t rows_off, minmax_off, counts_off, cand_off, bytes;
+  size_t rows_off, minmax_off, counts_off, cand_off, candk_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1483,7 +1523,8 @@ SplitLayout split_layout(const Batch& b) {
   L.minmax_off = align256(T * RW_WORDS * sizeof(uint32_t));
   L.counts_off = L.minmax_off + align256(T * L.max_chunks * sizeof(float2));
   L.cand_off = L.counts_off + align256(T * L.max_chunks * sizeof(uint2));
-  L.bytes = L.cand_off + align256(T * (size_t)L.cand_cap * sizeof(uint32_t));
+  L.candk_off = L.cand_off + align256(T * (size_t)L.cand_cap * sizeof(uint32_t));
+  L.bytes = L.candk_off + align256(T * (size_t)L.cand_cap * sizeof(uint32_t));
   return L;
 }
 
@@ -1502,6 +1543,7 @@ hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, 
   ws.minmax = (float2*)(base + L.minmax_off);
   ws.counts = (uint2*)(base + L.counts_off);
   ws.cand = (uint32_t*)(base + L.cand_off);
+  ws.candk = (uint32_t*)(base + L.candk_off);
   ws.max_chunks = L.max_chunks;
   ws.max_k = b.max_k;
   ws.cand_cap = L.cand_cap;
