@@ -119,7 +119,13 @@ dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, con
  *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 bytes / NULL when that is 0).
  *     It is non-zero for batches of at most 64 query rows whose longest sequence exceeds 32768
  *     keys: those rows are split over several workgroups that meet through per-row histograms
- *     and counts kept there. Its contents on entry do not matter; on return they are undefined.
+ *     and counts kept there. Its contents on entry do not matter (the call zero-fills what it
+ *     needs); on return they are undefined. For rows of at most 2,097,152 positions the row's
+ *     workgroups meet at barriers inside one launch (device-scope counters, polled): such a
+ *     barrier waits for workgroups of the same row only, which are dispatched before any later
+ *     row's, so it always completes once they can run; its polls are bounded (about a second),
+ *     so if other work kept a row's workgroups from running that long the launch still ends,
+ *     with that row's indices undefined. Longer rows take five launches.
  * Scores must not be NaN. */
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
                     int32_t index_topk, int32_t* indices, void* workspace, size_t ws_bytes,
@@ -221,7 +227,9 @@ typedef struct {
  * Per-position selection on the bf16 path with max_seqlen_k <= 16384 runs inside the sparse-MLA
  * launch (each attention workgroup selects its own slice of shared_indices from the score row),
  * so the top-k takes no launch of its own; shared_indices and the outputs are the same as with
- * the separate calls, bit for bit.
+ * the separate calls, bit for bit. When the top-k splits long rows over workgroups in one launch
+ * (see dsa_topk), the decode indexer launch zero-fills that launch's row state on the side, so
+ * the top-k is one launch here too.
  * The workspace holds the [T, max_seqlen_k] fp32 score matrix plus the selection and split-KV
  * scratch: dsa_workspace_size(DSA_OP_FORWARD, ...) bytes (enough for either selection). */
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_forward_args* args,

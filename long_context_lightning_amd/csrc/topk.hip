@@ -726,10 +726,10 @@ constexpr uint32_t SP_SPIN_LIMIT = 1u << 20;
 
 // Barrier of the workgroups of one row inside one launch, round `round` (1, 2, ..): each wave
 // waits until its own global stores and atomics have completed and the workgroup meets; then
-// one thread counts the workgroup in. Chunks are counted in eight groups (c % 8), so no single
-// word takes every arrival and every poll of a long row: the last arrival of a group counts the
-// group in, the last group sets every group's release word, and each workgroup polls only its
-// group's. Deadlock-free when every row's workgroups can be resident at once: workgroups are
+// one thread counts the workgroup in. Chunks of rows longer than 32 chunks are counted in eight
+// groups (c % 8), so no single word takes every arrival of a long row: the last arrival of a
+// group counts the group in, and the last group (or, in shorter rows, the last arrival) sets
+// every group's release word; each workgroup polls only its group's. Deadlock-free when every row's workgroups can be resident at once: workgroups are
 // dispatched in order, so the lowest unfinished row always has all its workgroups resident and
 // finishes.
 __device__ __forceinline__ void row_barrier(uint32_t* barw, int c, uint32_t n, uint32_t round) {
@@ -740,10 +740,16 @@ __device__ __forceinline__ void row_barrier(uint32_t* barw, int c, uint32_t n, u
     const uint32_t groups = min(n, 8u);
     const uint32_t in_group = (n + 7u - g) >> 3;
     uint32_t* release = barw + (9 + g) * BAR_STRIDE;
-    if (__hip_atomic_fetch_add(barw + g * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) + 1u == round * in_group &&
-        __hip_atomic_fetch_add(barw + 8 * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) + 1u == round * groups) {
+    // rows of at most 32 chunks count every arrival on the row's counter directly (one atomic
+    // round trip fewer); longer rows count groups first
+    const bool last =
+        n <= 32u ? __hip_atomic_fetch_add(barw + 8 * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) + 1u == round * n
+                 : (__hip_atomic_fetch_add(barw + g * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) + 1u == round * in_group &&
+                    __hip_atomic_fetch_add(barw + 8 * BAR_STRIDE, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) + 1u == round * groups);
+    if (last) {
       for (uint32_t j = 0; j < groups; ++j)
         __hip_atomic_store(barw + (9 + j) * BAR_STRIDE, round, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
