@@ -707,6 +707,39 @@ def test_topk_split_rows_beyond_one_launch():
     _crafted_topk(rows, 2048)
 
 
+def test_split_topk_on_a_garbage_workspace(monkeypatch):
+    """The one-launch split top-k zero-fills its row state before use: with every workspace
+    filled with 0xAB bytes, dsa_topk (its own clear launch) and dsa_forward (the decode indexer
+    clears the state on the side), each called twice in a row, give the oracle's top-k of the
+    GPU scores on every row, bit for bit, and dsa_forward's indices equal dsa_topk's."""
+    orig = dsa._workspace
+
+    def garbage(nbytes, device):
+        t, n = orig(nbytes, device)
+        if t is not None:
+            t.fill_(0xAB)
+        return t, n
+
+    monkeypatch.setattr(dsa, "_workspace", garbage)
+    case = _small_case("garbage_ws", (100000, 70001, 40000, 3000), (1, 1, 2, 1))
+    say("case", case.name)
+    d = DI.make_inputs(case, "cuda")
+    batch = batch_of(case, d)
+    scores = dsa.indexer_scores(d["q_idx"], d["k_idx"], d["w"], batch)
+    for _ in range(2):
+        idx = dsa.topk(scores, batch, case.index_topk)
+        out, lse, fidx = dsa.forward(d["q"][0], d["kv"][0], batch, case.index_topk,
+                                     case.softmax_scale, case.d_v, q_idx=d["q_idx"],
+                                     k_idx=d["k_idx"], w=d["w"])
+        torch.cuda.synchronize()
+        sc = scores.cpu().numpy()
+        got, fgot = idx.cpu().numpy(), fidx.cpu().numpy()
+        for t, b, p, base in DI.query_rows(case):
+            want = O.topk_row(sc[t, :p + 1].astype(np.float64), case.index_topk)
+            assert np.array_equal(got[t], want), ("dsa_topk", t)
+            assert np.array_equal(fgot[t], want), ("dsa_forward", t)
+
+
 def test_reference_max_restart_path():
     """Rows whose logits exceed the first tile's maximum by far more than the softmax headroom
     force the attention kernel to raise its reference maxima and redo the split; the result must
