@@ -120,8 +120,10 @@ dsa_status dsa_indexer_scores_fp8(const dsa_batch* batch, const void* q_idx, con
  *     It is non-zero for batches of at most 64 query rows whose longest sequence exceeds 32768
  *     keys: those rows are split over several workgroups that meet through per-row histograms
  *     and counts kept there. Its contents on entry do not matter (the call zero-fills what it
- *     needs); on return they are undefined. For rows of at most 2,097,152 positions the row's
- *     workgroups meet at barriers inside one launch (device-scope counters, polled): such a
+ *     needs); on return they are undefined. For rows of at most 2,097,152 positions, whose
+ *     workgroups the device can hold at once (its compute units times the kernel's occupancy,
+ *     queried once per device), the row's workgroups meet at barriers inside one launch
+ *     (device-scope counters, polled): such a
  *     barrier waits for workgroups of the same row only, which are dispatched before any later
  *     row's, so it always completes once they can run; its polls are bounded (about a second),
  *     so if other work kept a row's workgroups from running that long the launch still ends,

@@ -35,6 +35,9 @@
 //     each step of 256 positions ranks its taken positions with lane-mask counts.
 #include <algorithm>
 
+#include <map>
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1540,6 +1543,32 @@ bool use_split(const Batch& b, int k) {
   return b.max_k > 4 * TK_THREADS * 8 && b.max_k > k && b.total_q <= 64;
 }
 
+// Workgroups of topk_split_fused the current device holds at once (its compute units times the
+// kernel's occupancy per compute unit), found once per device: a row's barriers need all of the
+// row's workgroups resident, which a partitioned device with fewer compute units may not allow.
+int64_t fused_resident_capacity() {
+  static std::mutex mu;
+  static std::map<int, int64_t> cap;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cap.find(dev);
+  if (it != cap.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  int64_t c = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_split_fused, SP_THREADS, 0) ==
+          hipSuccess)
+    c = (int64_t)cus * per_cu;
+  cap[dev] = c;
+  return c;
+}
+
+// The one-launch path: rows of at most 256 chunks whose workgroups the device holds at once.
+bool one_launch_fits(int max_chunks) {
+  return max_chunks <= SP_THREADS && (int64_t)max_chunks <= fused_resident_capacity();
+}
+
 hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
                         void* workspace, bool state_zeroed, hipStream_t stream) {
   const SplitLayout L = split_layout(b);
@@ -1554,7 +1583,7 @@ hipError_t launch_split(const Batch& b, const float* scores, int64_t ld, int k, 
   ws.max_k = b.max_k;
   ws.cand_cap = L.cand_cap;
   const unsigned grid = (unsigned)((int64_t)b.total_q * L.max_chunks);
-  if (L.max_chunks <= SP_THREADS) {
+  if (one_launch_fits(L.max_chunks)) {
     // one launch once the row state is zero: at most 64 rows of at most 256 chunks are 16384
     // workgroups of 256 threads, of which one row's (at most 256) are always resident
     const int64_t words = (int64_t)b.total_q * RW_WORDS;
@@ -1594,7 +1623,7 @@ size_t topk_workspace_bytes(const Batch& b, int k) {
 int64_t topk_state_words(const Batch& b, int k) {
   if (!use_split(b, k)) return 0;
   const SplitLayout L = split_layout(b);
-  return L.max_chunks <= SP_THREADS ? (int64_t)b.total_q * RW_WORDS : 0;
+  return one_launch_fits(L.max_chunks) ? (int64_t)b.total_q * RW_WORDS : 0;
 }
 
 hipError_t launch_topk(const Batch& b, const float* scores, int64_t ld, int k, int32_t* indices,
